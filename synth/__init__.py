@@ -29,6 +29,8 @@ Named workloads (sizes of one expert-parallel rank's share):
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
 
 CONFIGS = {
@@ -63,16 +65,29 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def bf16_normal(rng: np.random.Generator, shape, std: float, chunk: int = 1 << 24) -> np.ndarray:
-    """N(0, std) rounded to bf16, as uint16 bits; drawn in chunks to bound memory."""
+def bf16_normal(seed: int, stream: int, shape, std: float, chunk: int = 1 << 22) -> np.ndarray:
+    """N(0, std) rounded to bf16, as uint16 bits. Chunk i is drawn from its own
+    generator (seed, stream, i), so the values do not depend on how many threads
+    fill the chunks."""
     n = int(np.prod(shape))
     out = np.empty(n, np.uint16)
-    for i in range(0, n, chunk):
+
+    def fill(i):
         m = min(chunk, n - i)
-        v = rng.standard_normal(m, dtype=np.float32)
+        v = np.random.default_rng([int(seed), int(stream), i // chunk]).standard_normal(
+            m, dtype=np.float32)
         if std != 1.0:
             v *= np.float32(std)
         out[i:i + m] = f32_to_bf16_bits(v)
+
+    starts = range(0, n, chunk)
+    if n > 4 * chunk:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+            list(ex.map(fill, starts))
+    else:
+        for i in starts:
+            fill(i)
     return out.reshape(shape)
 
 
@@ -187,11 +202,11 @@ def make_inputs(name_or_cfg, seed: int = 0, dout: bool = True, topk_idx=None,
     topk_idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
     d = dict(cfg=cfg, seed=used, N=N, H=H, I=I, E=E, K=K, topk_idx=topk_idx,
              topk_weights=make_topk_weights(topk_idx, used),
-             x=bf16_normal(_rng(used, _S_X), (N, H), 1.0),
-             w_up=bf16_normal(_rng(used, _S_WUP), (E, H, 2 * I), w_std),
-             w_down=bf16_normal(_rng(used, _S_WDOWN), (E, I, H), w_std))
+             x=bf16_normal(used, _S_X, (N, H), 1.0),
+             w_up=bf16_normal(used, _S_WUP, (E, H, 2 * I), w_std),
+             w_down=bf16_normal(used, _S_WDOWN, (E, I, H), w_std))
     if dout:
-        d["dout"] = bf16_normal(_rng(used, _S_DOUT), (N, H), 1.0)
+        d["dout"] = bf16_normal(used, _S_DOUT, (N, H), 1.0)
     return d
 
 

@@ -1,0 +1,65 @@
+"""The C ABI library loads and exports every function include/*.h declares, and
+rejects bad arguments synchronously (no GPU needed: these paths enqueue nothing)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w \*]*?\b(moe_\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_exports_every_declared_symbol():
+    import token_routing_grouped_amd as moe
+    names = declared_functions()
+    assert {"moe_build_metadata", "moe_expert_forward", "moe_expert_backward"} <= names
+    L = moe.lib()
+    for n in sorted(names):
+        assert hasattr(L, n), f"libmoe.so does not export {n}"
+    assert set(moe.EXPORTED_SYMBOLS) == names
+
+
+def test_synchronous_argument_errors():
+    import token_routing_grouped_amd as moe
+    from token_routing_grouped_amd._binding import _CMeta
+    L = moe.lib()
+    assert moe.moe_status_string(0) == "ok"
+    # null metadata
+    assert L.moe_build_metadata(None, None, None, None, 0, None) == 1
+    # a struct with bad sizes, all pointers null
+    m = _CMeta(4, 0, 3, 8, *([None] * 8))
+    assert L.moe_build_metadata(None, None, ctypes.byref(m), None, 0, None) == 1
+    m = _CMeta(4, 2, 3, 8, *([16] * 8))  # fake non-null device addresses; never dereferenced
+    # short workspace
+    need = L.moe_build_metadata_workspace(4, 2, 3)
+    assert need > 0
+    assert L.moe_build_metadata(16, 16, ctypes.byref(m), 16, need - 1, None) == 2
+    # unsupported shapes and dtypes
+    assert L.moe_expert_forward(ctypes.byref(m), 16, 16, 16, 100, 128, 0, 0, None, 16, 16,
+                                1 << 30, None) == 3
+    assert L.moe_expert_forward(ctypes.byref(m), 16, 16, 16, 128, 128, 7, 0, None, 16, 16,
+                                1 << 30, None) == 3
+    assert L.moe_expert_forward(ctypes.byref(m), 16, 16, 16, 128, 128, 0, 1, None, 16, 16,
+                                1 << 30, None) == 3
+    # short forward / backward workspace
+    fneed = L.moe_expert_forward_workspace(ctypes.byref(m), 128, 128, 0)
+    assert L.moe_expert_forward(ctypes.byref(m), 16, 16, 16, 128, 128, 0, 0, None, 16, 16,
+                                fneed - 1, None) == 2
+    bneed = L.moe_expert_backward_workspace(ctypes.byref(m), 128, 128, 0)
+    assert bneed > fneed
+    assert L.moe_expert_backward(ctypes.byref(m), 16, 16, 16, 16, 16, 16, 128, 128, 0, 0,
+                                 16, 16, 16, 16, 16, bneed - 1, None) == 2
+    # missing saved activations
+    assert L.moe_expert_backward(ctypes.byref(m), 16, 16, 16, 16, None, 16, 128, 128, 0, 0,
+                                 16, 16, 16, 16, 16, bneed, None) == 1

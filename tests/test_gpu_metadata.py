@@ -1,0 +1,100 @@
+"""GPU routing metadata vs the oracle: bit-exact on every workload and edge case.
+
+The seven arrays are the ones GitHub issue #68 on Dao-AILab/sonic-moe lists; with
+token-major pairs and a stable sort by expert they are unique, so the HIP path
+must reproduce the oracle exactly (integer work: bit-exact; router_scores are
+copies of fp32 inputs: bit-exact too).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from _util import Gpu
+
+pytestmark = pytest.mark.gpu
+
+KEYS = ["expert_frequency", "expert_frequency_offset", "x_gather_idx", "s_scatter_idx",
+        "s_reverse_scatter_idx", "num_activated_expert_per_token_offset", "router_scores"]
+PAIR_KEYS = {"x_gather_idx", "s_scatter_idx", "s_reverse_scatter_idx", "router_scores"}
+
+
+def check(idx, w, E, capacity=None, expect_status=0):
+    N, K = idx.shape
+    d = dict(N=N, H=128, I=128, E=E, K=K, topk_idx=np.ascontiguousarray(idx, np.int32),
+             topk_weights=np.ascontiguousarray(w, np.float32),
+             x=np.zeros((N, 128), np.uint16), w_up=np.zeros((E, 128, 256), np.uint16),
+             w_down=np.zeros((E, 128, 128), np.uint16))
+    print(f"metadata case N={N} K={K} E={E} capacity={capacity}", flush=True)
+    g = Gpu(d, capacity=capacity)
+    g.build()
+    got = g.meta_numpy()
+    ref = oracle.build_metadata(idx, w, E)
+    assert got["P"] == ref["P"]
+    n = min(ref["P"], g.meta.capacity)
+    for k in KEYS:
+        r = ref[k]
+        if k in PAIR_KEYS:  # entries at positions >= capacity are dropped
+            r = r[:n]
+        a = got[k]
+        assert a.shape == r.shape, k
+        assert np.array_equal(a, r.astype(a.dtype)), f"{k} differs"
+    assert got["status"] == expect_status
+    return got
+
+
+@pytest.mark.parametrize("name", list(synth.CONFIGS))
+def test_workloads(name):
+    idx, seed = synth.make_routing(name, 0)
+    w = synth.make_topk_weights(idx, seed)
+    check(idx, w, synth.CONFIGS[name]["E"])
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("N,K,E,p", [(1, 1, 1, 0.0), (3, 2, 3, 0.3), (1000, 8, 64, 0.5),
+                                     (4097, 6, 17, 0.2), (2048, 1, 1, 0.1),
+                                     (3000, 16, 1024, 0.0), (50000, 3, 5, 0.9)])
+def test_random(N, K, E, p, seed):
+    rng = np.random.default_rng(seed)
+    idx = rng.integers(0, E, size=(N, K)).astype(np.int32)  # duplicates in a row allowed
+    idx[rng.random((N, K)) < p] = -1
+    w = rng.standard_normal((N, K)).astype(np.float32)
+    check(idx, w, E)
+
+
+def test_all_invalid_and_empty():
+    check(-np.ones((100, 4), np.int32), np.zeros((100, 4), np.float32), 8)
+    check(np.zeros((0, 4), np.int32), np.zeros((0, 4), np.float32), 8)
+
+
+def test_capacity_larger_than_P():
+    idx, seed = synth.make_routing("tiny", 0)
+    w = synth.make_topk_weights(idx, seed)
+    check(idx, w, 8, capacity=idx.size)
+
+
+def test_over_capacity_sets_status():
+    idx, seed = synth.make_routing("tiny", 0)
+    w = synth.make_topk_weights(idx, seed)
+    P = int((idx >= 0).sum())
+    check(idx, w, 8, capacity=P - 7, expect_status=2)
+
+
+def test_bad_expert_ids_set_status():
+    rng = np.random.default_rng(9)
+    idx = rng.integers(-1, 8, size=(300, 4)).astype(np.int32)
+    idx[5, 1] = 8
+    idx[17, 0] = -3
+    w = rng.standard_normal((300, 4)).astype(np.float32)
+    got = check(np.where((idx >= -1) & (idx < 8), idx, -1), w, 8)
+    # the same input with the bad ids: treated as -1, flagged
+    N, K = idx.shape
+    d = dict(N=N, H=128, I=128, E=8, K=K, topk_idx=idx, topk_weights=w,
+             x=np.zeros((N, 128), np.uint16), w_up=np.zeros((8, 128, 256), np.uint16),
+             w_down=np.zeros((8, 128, 128), np.uint16))
+    g = Gpu(d, capacity=got["P"])
+    g.build()
+    bad = g.meta_numpy()
+    assert bad["status"] == 1
+    for k in KEYS:
+        assert np.array_equal(bad[k], got[k]), k

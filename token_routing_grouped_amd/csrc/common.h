@@ -1,0 +1,81 @@
+// Device helpers shared by the gfx950 kernels of the local MoE expert layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kWave = 64;
+constexpr int kNumXcd = 8;  // gfx950: workgroups are dealt round-robin to 8 XCDs
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+// fp32 -> bf16, round to nearest even (the language conversion; gfx950 has it in hardware)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 h = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ int lane_id() {
+  return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0));
+}
+// number of set bits of m at lanes below the calling lane
+__device__ __forceinline__ int popc_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+}
+__device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
+
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// In-place exclusive scan of a[0..n) in LDS by wave 0 of the block (n <= 64*16).
+// Writes the total to a[n]. Caller synchronises before and after.
+__device__ __forceinline__ void wave0_exclusive_scan(int *a, int n) {
+  if (threadIdx.x >= kWave) return;
+  const int lane = threadIdx.x;
+  const int per = (n + kWave - 1) / kWave;
+  const int lo = lane * per;
+  const int hi = lo + per < n ? lo + per : n;
+  int s = 0;
+  for (int i = lo; i < hi; i++) s += a[i];
+  const int incl = wave_inclusive_scan(s);
+  int run = incl - s;
+  for (int i = lo; i < hi; i++) {
+    const int v = a[i];
+    a[i] = run;
+    run += v;
+  }
+  if (lane == kWave - 1) a[n] = incl;
+}
+
+// Bijection of hardware workgroup ids [0,G) onto logical ids so that each XCD
+// (hardware id modulo 8) receives one contiguous range of logical ids: work that
+// shares operands lands on the same L2.
+__device__ __forceinline__ int xcd_chunked(int b, int G) {
+  const int x = b % kNumXcd, i = b / kNumXcd;
+  const int q = G / kNumXcd, r = G % kNumXcd;
+  return x * q + (x < r ? x : r) + i;
+}
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+__device__ __forceinline__ float sigmoid_f(float g) { return 1.0f / (1.0f + __expf(-g)); }
+
+}  // namespace moe

@@ -1,0 +1,85 @@
+// Host-side launchers of the gfx950 kernels (internal to libmoe).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- routing metadata -------------------------------------------------------
+constexpr int kMetaThreads = 256;
+constexpr int kMetaItems = 8;                           // slots per thread
+constexpr int kMetaChunk = kMetaThreads * kMetaItems;  // slots per workgroup
+
+struct MetaOut {
+  int32_t *expert_frequency, *expert_frequency_offset, *x_gather_idx, *s_scatter_idx,
+      *s_reverse_scatter_idx, *tok_off;
+  float *router_scores;
+  uint32_t *status;
+};
+
+inline int meta_blocks(int64_t NK) {
+  int64_t b = (NK + kMetaChunk - 1) / kMetaChunk;
+  return b < 1 ? 1 : (int)b;
+}
+inline size_t meta_workspace_bytes(int64_t NK, int E) {
+  return (size_t)meta_blocks(NK) * (size_t)(E + 1) * sizeof(int32_t);
+}
+hipError_t launch_meta_hist(const int32_t *topk_idx, int N, int K, int E, int32_t *hist_ws,
+                            hipStream_t stream);
+hipError_t launch_meta_scatter(const int32_t *topk_idx, const float *topk_weights, int N, int K,
+                               int E, int capacity, const int32_t *hist_ws, const MetaOut &out,
+                               hipStream_t stream);
+
+// ---- grouped GEMMs (bf16 MFMA) ----------------------------------------------
+// Two schedules:
+//  grouped-M: C[s,:] = A[row(s),:] B_e for the rows s of each expert segment
+//             (M varies per expert, N and K fixed);
+//  varlen-K:  C_e = sum over the segment's rows s of A[row(s),:]^T B[row(s),:]
+//             (M and N fixed, the reduction length varies per expert).
+enum GemmKind {
+  kUpSwiGLU = 0,   // h = x_g W_up (B [K][N]); epilogue writes h and a = silu(g)*u
+  kDown = 1,       // y = a W_down (B [K][N])
+  kDownBwd = 2,    // da_u = dout_g W_down^T (B [N][K]); epilogue: dSwiGLU, dscore partials
+  kUpBwd = 3,      // dxg = dh W_up^T (B [N][K])
+  kWeightGrad = 4  // varlen-K: dW_e = A_g^T B_g (both row-major over the segment)
+};
+
+struct GemmArgs {
+  const int32_t *foff;  // [E+1] segment offsets of the sorted positions
+  int E, cap;
+  int M, N, K;  // grouped-M uses N, K; varlen-K uses M, N
+  const void *A;
+  int64_t lda, a_es;
+  const int32_t *a_rows;  // row map (gather) or null = identity
+  const void *B;
+  int64_t ldb, b_es;
+  const int32_t *b_rows;
+  void *C;
+  int64_t ldc, c_es;
+  void *C2;  // kUpSwiGLU: a [cap,I]; kDownBwd: w*a [cap,I]
+  int64_t ldc2;
+  const void *Hs;  // kDownBwd: saved h [cap,2I]
+  int64_t ldh;
+  const float *scores;       // router_scores [cap] (pair order)
+  const int32_t *s_scatter;  // s -> q
+  float *partial;            // kDownBwd: [cap, n_ntiles] per-tile partial dscore
+  int n_ntiles;
+};
+
+constexpr int kGemmBM = 128, kGemmBN = 128, kGemmBK = 64;
+int gemm_grid(GemmKind kind, const GemmArgs &g);
+hipError_t launch_gemm_bf16(GemmKind kind, const GemmArgs &g, hipStream_t stream);
+hipError_t launch_gemm_f32(GemmKind kind, const GemmArgs &g, hipStream_t stream);
+
+// ---- combine and router-weight gradient --------------------------------------
+// out[t,:] = sum over the token's pairs q (ascending) of w_q * y[s_rev[q],:]
+// (w_q = 1 when scores is null); fp32 accumulation, one rounding.
+hipError_t launch_combine(bool bf16, const void *y, const int32_t *tok_off,
+                          const int32_t *s_rev, const float *scores, int N, int H, int cap,
+                          void *out, hipStream_t stream);
+// d_topk_weights[t,k] = sum over tiles of partial[s_rev[q],tile] at valid slots, else 0.
+hipError_t launch_dscore(const int32_t *topk_idx, int N, int K, int E, const int32_t *tok_off,
+                         const int32_t *s_rev, const float *partial, int n_ntiles, int cap,
+                         float *d_topk_weights, hipStream_t stream);
+
+}  // namespace moe
