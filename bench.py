@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Benchmark of the local MoE expert layer on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input resident in HBM:
+routing metadata from topk_idx/topk_weights [N,K], the forward (gathered
+up-projection + SwiGLU, down projection, weighted combine), and the backward
+(dx, dW_up, dW_down, d_topk_weights). The default workload is one EP8 rank's
+share of a 256-expert top-8 layer: N=16384 received rows, H=2048, I=512, E=32
+local experts, K=8 (the Qwen3.6 serving-script notes: 256 experts x top-8 at
+16384 tokens; GitHub issue #68: EP8 with DeepEP non-expand inputs).
+
+Prints one JSON line: throughput in TFLOP/s over valid pairs (18*P*H*I per
+forward+backward step), the routing-metadata build time and its fraction of
+HBM bandwidth, the dominant kernel against its roofline (timed with HIP events
+on its own stream through the library's kernel-timing hook), and the CPU oracle
+timed on a bounded sample of the same workload on this host.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("MoE expert fwd+bwd TFLOP/s and % bf16 MFMA peak; metadata build µs, "
+          "% HBM BW")
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
+
+# algorithmic flops of each GEMM kernel per launch, in units of P*H*I
+GEMM_FLOPS = {"up_swiglu": 4, "down": 2, "down_bwd": 2, "wgrad_down": 2, "up_bwd": 4,
+              "wgrad_up": 4}
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "token_routing_grouped_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counted_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken on
+    the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    ent = rec.get(workload, {}).get(kernel)
+    if not ent or ent.get("source_digest") != source_digest():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(d, backward: bool, target_s: float):
+    """The oracle (fp64, OpenMP) on the first tokens of the workload: metadata,
+    forward and (if the workload has it) backward, on full tensors of that sample."""
+    import numpy as np
+
+    import oracle
+
+    f64 = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    wu, wd = f64(d["w_up"]), f64(d["w_down"])
+    idx, w = d["topk_idx"], d["topk_weights"]
+    H, I, E = d["H"], d["I"], d["E"]
+    valid = (idx >= 0).sum(axis=1)
+    csum = np.cumsum(valid)
+    mult = (18 if backward else 6) * H * I
+
+    def run(pairs):
+        n = int(np.searchsorted(csum, pairs)) + 1
+        n = min(n, idx.shape[0])
+        t0 = time.perf_counter()
+        m = oracle.build_metadata(idx[:n], w[:n], E)
+        x = f64(d["x"][:n])
+        f = oracle.forward(x, wu, wd, m)
+        if backward:
+            oracle.backward(x, wu, wd, f64(d["dout"][:n]), m, f)
+        return n, m["P"], time.perf_counter() - t0
+
+    n, P, t = run(512)  # calibration
+    rate = P * mult / max(t, 1e-6)
+    want = int(min(csum[-1], max(512, target_s * rate / mult)))
+    n, P, t = run(want)
+    t0 = time.perf_counter()
+    oracle.build_metadata(idx, w, E)
+    t_meta = time.perf_counter() - t0
+    return {
+        "value": P * mult / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"first {n} of {idx.shape[0]} rows ({P} pairs): metadata + forward"
+                   f"{' + backward' if backward else ''} in fp64, {t:.1f} s"),
+        "metadata_us_full_workload": t_meta * 1e6,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_rank")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="instead of the benchmark, run a plain device copy of this many MiB "
+                         "(reference kernel for scaling HBM traffic counters)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one rank's local expert layer on one GPU; --gpus {args.gpus} "
+              f"(WORLD_SIZE={world}) is not supported in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.copy_mib:
+        src = torch.ones(args.copy_mib << 20, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_mib << 20, "launches": 3}))
+        return
+
+    import synth
+    import token_routing_grouped_amd as moe
+
+    cfg = synth.CONFIGS[args.workload]
+    backward = cfg["backward"]
+    d = synth.make_inputs(args.workload, args.seed, dout=backward)
+    N, H, I, E, K = d["N"], d["H"], d["I"], d["E"], d["K"]
+    P = int((d["topk_idx"] >= 0).sum())
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    def t(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x, w_up, w_down = t(d["x"]), t(d["w_up"]), t(d["w_down"])
+    dout = t(d["dout"]) if backward else None
+    idx = torch.from_numpy(d["topk_idx"]).to(dev)
+    w = torch.from_numpy(d["topk_weights"]).to(dev)
+    # capacity = P, known on the host as DeepEP's handle knows total_pairs
+    meta = moe.Metadata(N, K, E, P, device=dev)
+    u8 = dict(dtype=torch.uint8, device=dev)
+    ws_meta = torch.empty(max(1, moe.moe_build_metadata_workspace(N, K, E)), **u8)
+    ws_fwd = torch.empty(max(1, moe.moe_expert_forward_workspace(meta, H, I)), **u8)
+    ws_bwd = torch.empty(max(1, moe.moe_expert_backward_workspace(meta, H, I)), **u8)
+    out = torch.empty(N, H, dtype=torch.bfloat16, device=dev)
+    h_save = torch.empty(P, 2 * I, dtype=torch.bfloat16, device=dev) if backward else None
+    if backward:
+        dx = torch.empty_like(x)
+        dw_up = torch.empty_like(w_up)
+        dw_down = torch.empty_like(w_down)
+        dtw = torch.empty(N, K, dtype=torch.float32, device=dev)
+
+    def build():
+        moe.moe_build_metadata(idx, w, meta, workspace=ws_meta)
+
+    def step():
+        build()
+        moe.moe_expert_forward(meta, x, w_up, w_down, out, h_save=h_save, workspace=ws_fwd)
+        if backward:
+            moe.moe_expert_backward(meta, idx, x, w_up, w_down, h_save, dout, dx, dw_up,
+                                    dw_down, dtw, workspace=ws_bwd)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    status = int(meta.status.item())
+    assert status == 0, f"device status {status}"
+    assert torch.isfinite(out.float()).all()
+
+    # per-kernel durations (3 launches each) to name the dominant kernel
+    kernels = moe.KERNELS if backward else moe.KERNELS[:5]
+    kernel_us = {}
+    for k in kernels:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        moe.moe_time_kernel(k, ev)
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        moe.moe_time_kernel(k, None)
+        kernel_us[k] = 1e3 * sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(3)) / 3
+    gemms = {k: v for k, v in kernel_us.items() if k in GEMM_FLOPS}
+    dominant = max(gemms, key=gemms.get)
+
+    # metadata build alone: back-to-back calls, events around the loop
+    nm = 50
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(nm):
+        build()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    meta_us = 1e3 * e0.elapsed_time(e1) / nm
+    meta_bytes = 8 * N * K + 16 * P + 4 * (N + 1) + 4 * E + 4 * (E + 1)
+
+    # timed region: K steps, the dominant kernel bracketed on its stream
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    moe.moe_time_kernel(dominant, ev)
+    wall0 = time.perf_counter()
+    s0.record(stream)
+    for _ in range(args.steps):
+        step()
+    s1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    nrec = moe.moe_time_kernel(dominant, None)
+    assert nrec == args.steps, nrec
+    ms = s0.elapsed_time(s1) / args.steps
+    dom_ms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)) / args.steps
+    assert int(meta.status.item()) == 0
+
+    flops_step = (18 if backward else 6) * P * H * I
+    tflops = flops_step / (ms * 1e-3) / 1e12
+    dom_flops = GEMM_FLOPS[dominant] * P * H * I
+    dom_tflops = dom_flops / (dom_ms * 1e-3) / 1e12
+    traffic = counted_traffic(dominant, args.workload)
+
+    res = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "N": N, "H": H, "I": I, "E": E, "K": K, "P": P,
+                   "seed": d["seed"],
+                   "step": "metadata + forward" + (" + backward" if backward else ""),
+                   "flops_per_step": flops_step},
+        "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "metadata": {"us": round(meta_us, 2), "bytes": meta_bytes,
+                     "GBps": round(meta_bytes / (meta_us * 1e-6) / 1e9, 1),
+                     "hbm_frac": round(meta_bytes / (meta_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)},
+        "kernels_us": {k: round(v, 1) for k, v in kernel_us.items()},
+        "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(dom_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "avg_us": round(dom_ms * 1e3, 2),
+                     "flops_per_launch": dom_flops},
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(d, backward, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -160,7 +160,8 @@ typedef enum {
 /* After this call, the i-th launch of `kernel` (i < n_launches, counted from this
  * call) is bracketed by hipEventRecord(events[2i]) just before it and
  * hipEventRecord(events[2i+1]) just after it, on the launch's stream. events
- * holds 2*n_launches hipEvent_t created by the caller; events == NULL stops
+ * holds 2*n_launches hipEvent_t created by the caller (none NULL, else
+ * MOE_EINVAL); events == NULL stops
  * recording. Process-wide state, not thread-safe; for benchmarks only.
  * Returns the number of launches bracketed since the previous call through
  * *n_recorded (may be NULL). */

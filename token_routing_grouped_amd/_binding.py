@@ -236,6 +236,9 @@ def moe_time_kernel(kernel, events=None) -> int:
         _check(lib().moe_time_kernel(int(kernel), None, 0, ctypes.byref(n)), "moe_time_kernel")
         return n.value
     assert len(events) % 2 == 0
+    for e in events:
+        if not e.cuda_event:  # torch creates the HIP event on its first record
+            e.record()
     arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
     _keep_alive.append(arr)
     _check(lib().moe_time_kernel(int(kernel), arr, len(events) // 2, ctypes.byref(n)),

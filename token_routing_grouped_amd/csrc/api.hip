@@ -306,6 +306,8 @@ moe_status moe_time_kernel(moe_kernel_id kernel, void *const *events, int32_t n_
   if (n_recorded) *n_recorded = g_hook.i;
   if (events && ((int)kernel < 0 || (int)kernel >= MOE_KERNEL_COUNT || n_launches < 0))
     return MOE_EINVAL;
+  for (int i = 0; events && i < 2 * n_launches; i++)
+    if (!events[i]) return MOE_EINVAL;
   g_hook.kernel = (int)kernel;
   g_hook.events = (hipEvent_t const *)events;
   g_hook.n = events ? n_launches : 0;
