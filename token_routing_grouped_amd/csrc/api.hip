@@ -94,7 +94,7 @@ GemmArgs base_args(const moe_metadata *m) {
 
 moe_status gemm(GemmKind kind, moe_kernel_id id, const GemmArgs &g, moe_dtype dt,
                 hipStream_t st) {
-  if (gemm_grid(kind, g) < 0) return MOE_EUNSUPPORTED;
+  if ((dt == MOE_BF16 ? gemm_grid(kind, g) : gemm_grid_f32(kind, g)) < 0) return MOE_EUNSUPPORTED;
   Bracket b(id, st);
   hipError_t err = dt == MOE_BF16 ? launch_gemm_bf16(kind, g, st) : launch_gemm_f32(kind, g, st);
   return err == hipSuccess ? MOE_OK : MOE_EHIP;
@@ -223,7 +223,6 @@ moe_status moe_expert_backward(const moe_metadata *meta, const int32_t *topk_idx
   char *ws = (char *)workspace;
   void *dh = ws + L.dh, *aw = ws + L.aw, *dxg = ws + L.dxg;
   float *partial = (float *)(ws + L.partial);
-  const int nnt = I / kGemmBN;
 
   // da_u = dout_g W_down^T; epilogue: dh, w*a, per-tile dscore partials
   GemmArgs g = base_args(meta);
@@ -244,7 +243,14 @@ moe_status moe_expert_backward(const moe_metadata *meta, const int32_t *topk_idx
   g.scores = meta->router_scores;
   g.s_scatter = meta->s_scatter_idx;
   g.partial = partial;
-  g.n_ntiles = nnt;
+  if (dt == MOE_BF16) {  // one dscore partial per column tile of this GEMM
+    int bm, bn;
+    gemm_tile(kDownBwd, g, &bm, &bn);
+    g.n_ntiles = I / bn;
+  } else {
+    g.n_ntiles = I / kGemmBN;
+  }
+  const int nnt = g.n_ntiles;
   moe_status s = MOE_OK;
   if (meta->N > 0 && (s = gemm(kDownBwd, MOE_KERNEL_DOWN_BWD, g, dt, st)) != MOE_OK) return s;
   // dW_down[e] = (w a)^T dout_g over the expert's rows

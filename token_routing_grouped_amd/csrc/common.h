@@ -10,6 +10,10 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+// 16 bytes as a native vector (HIP's uint4 struct is copied through memory by the
+// optimizer; a native vector stays in registers)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kNumXcd = 8;  // gfx950: workgroups are dealt round-robin to 8 XCDs

@@ -5,26 +5,28 @@
 // one F.linear per expert because variable-size GEMMs cannot be batched there;
 // GitHub issue #68 keeps SonicMoE's grouped GEMM for the expert compute. Here one
 // launch covers every expert:
-//  - grouped-M: a workgroup owns a 128x128 output tile of one expert segment.
-//    It reads the segment offsets (expert_frequency_offset), counts
-//    ceil(freq_e/128) row tiles per expert, and finds its (expert, first row,
-//    column tile) itself, so the grid is sized from the capacity alone and no
-//    host sync is needed; surplus workgroups exit. Partial row tiles are padded
-//    with zeros in LDS, never in memory. The A rows are gathered through a row
-//    map (x_gather_idx) directly in the tile load.
-//  - varlen-K (weight gradients): a workgroup owns a 128x128 tile of one
-//    expert's gradient and reduces over that expert's rows; empty experts write
-//    exact zeros.
+//  - grouped-M: a workgroup owns a BMxBN output tile of one expert segment. It
+//    reads the segment offsets (expert_frequency_offset), counts ceil(freq_e/BM)
+//    row tiles per expert, and finds its (expert, first row, column tile) itself,
+//    so the grid is sized from the capacity alone and no host sync is needed;
+//    surplus workgroups exit. Partial row tiles are padded with zeros in LDS,
+//    never in memory. A rows are gathered through a row map (x_gather_idx)
+//    directly in the tile load.
+//  - varlen-K (weight gradients): a workgroup owns a BMxBN tile of one expert's
+//    gradient and reduces over that expert's rows; empty experts write zeros.
 // Workgroup ids are regrouped so that each of the 8 XCDs runs a contiguous run
-// of tiles (tiles of one expert share weights, consecutive column tiles share
-// the gathered rows), which keeps the reuse inside one L2.
+// of tiles (tiles of one expert share weights, consecutive column tiles share the
+// gathered rows), which keeps the reuse inside one L2.
 //
-// Tile: 128x128x64, 256 threads = 2x2 waves of 64x64, each wave 2x2
-// v_mfma_f32_32x32x16_bf16. LDS holds two stages of an A and a B tile. Operands
-// whose reduction index is contiguous in memory are stored [rows][64+8] and read
-// with 16-byte LDS loads; operands contiguous along M or N are stored as loaded,
-// [64][128+16], and read with ds_read_b64_tr_b16 (transposing LDS reads), so no
-// operand is transposed in registers.
+// Tiles: BM x BN x 64 with BM, BN in {128, 256}; 256 threads = 2x2 waves, each
+// wave (BM/2)x(BN/2) built from v_mfma_f32_32x32x16_bf16. LDS holds two stages of
+// an A and a B tile. Operands whose reduction index is contiguous in memory are
+// stored [rows][64+8] and read with 16-byte LDS loads; operands contiguous along
+// M or N are stored as loaded, [64][cols+32], and read with ds_read_b64_tr_b16
+// (transposing LDS reads), so no operand is transposed in registers. The +32
+// padding puts the four rows a 16-lane group reads, and the two groups served
+// together, on disjoint banks. Plain stores go through LDS so every row leaves
+// as whole 128-byte lines.
 #include "common.h"
 #include "kernels.h"
 #include "../../include/moe.h"
@@ -32,39 +34,54 @@
 namespace moe {
 namespace {
 
-constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK, NT = 256;
-constexpr int LDK = BK + 8;    // row stride of a reduction-contiguous tile [128][BK]
-constexpr int LDC = 128 + 16;  // row stride of an M/N-contiguous tile [BK][128]
-constexpr int TILE = 128 * LDK;
-static_assert(BK * LDC == TILE, "both tile kinds take the same LDS");
+constexpr int BK = kGemmBK, NT = 256;
+constexpr int LDK = BK + 8;  // row stride of a reduction-contiguous tile [rows][BK]
+constexpr int PADC = 32;     // extra columns of an M/N-contiguous tile [BK][cols]
 
 enum { GROUPED_M = 0, VARLEN_K = 1 };
 enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_DSWIGLU = 2 };
 
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 
+template <bool KC, int R>
+struct TileShape {  // elements of one LDS stage of an operand with R rows (M or N)
+  static constexpr int ld = KC ? LDK : R + PADC;
+  static constexpr int elems = KC ? R * LDK : BK * (R + PADC);
+};
+
 __device__ __forceinline__ bf16x8 frag_kc(const uint16_t *tile, int r, int kk) {
-  return __builtin_bit_cast(bf16x8, *(const uint4 *)(tile + r * LDK + kk));
+  return __builtin_bit_cast(bf16x8, *(const u32x4 *)(tile + r * LDK + kk));
 }
 
-// B (or A) operand of v_mfma_f32_32x32x16_bf16 from a [k][col] tile: lane l needs
-// rows kbase + (l/32)*8 + 0..7 of column cbase + l%32. One ds_read_b64_tr_b16 gives
-// each lane of a 16-lane group 4 consecutive rows of one column when lane j of the
-// group points at row k0 + j/4, columns c0 + (j%4)*4 .. +3.
+// Operand of v_mfma_f32_32x32x16_bf16 from a [k][col] tile with row stride ld:
+// lane l needs rows kbase + (l/32)*8 + 0..7 of column cbase + l%32. One
+// ds_read_b64_tr_b16 gives each lane of a 16-lane group 4 consecutive rows of one
+// column when lane j of the group points at row k0 + j/4, columns c0 + (j%4)*4 ..+3.
+template <int LD>
 __device__ __forceinline__ bf16x8 frag_mn(const uint16_t *tile, int kbase, int cbase, int lane) {
   const int g = lane >> 4, j = lane & 15;
   const int c = cbase + (g & 1) * 16 + (j & 3) * 4;
   const int k = kbase + (g >> 1) * 8 + (j >> 2);
-  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(tile + k * LDC + c));
-  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(tile + (k + 4) * LDC + c));
+  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(tile + k * LD + c));
+  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(tile + (k + 4) * LD + c));
   i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, v);
 }
 
-template <int MODE, bool A_KC, bool B_KC, int EPI>
-__global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];  // [stage][A | B]
-  __shared__ int s_pref[MOE_MAX_EXPERTS + 2];
+template <int MODE, bool A_KC, bool B_KC, int EPI, int BM, int BN>
+__global__ __launch_bounds__(NT, (BM * BN <= 128 * 128) ? 2 : 1) void gemm_bf16_kernel(GemmArgs g) {
+  constexpr int TM = BM / 64, TN = BN / 64;  // 32x32 sub-tiles per wave
+  constexpr int WM = BM / 2, WN = BN / 2;    // wave tile
+  using AS = TileShape<A_KC, BM>;
+  using BS = TileShape<B_KC, BN>;
+  constexpr int STAGE = AS::elems + BS::elems;
+  constexpr int CLD = BN + 8;  // C staging row stride (elements)
+  static_assert(BM * CLD <= 2 * STAGE, "C staging fits in the stage buffers");
+  static_assert(2 * STAGE * 2 >= (MOE_MAX_EXPERTS + 2) * 4, "tile table fits");
+  constexpr int A_LD = BM / 32;  // 16-byte chunks per thread per stage
+  constexpr int B_LD = BN / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+  int *s_pref = (int *)smem;  // expert tile table, used before the first stage is written
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -94,6 +111,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmArgs g) {
     row0 = g.foff[e] + (mtile - s_pref[e]) * BM;
     rows = min(BM, g.foff[e + 1] - row0);
     nk = g.K / BK;
+    __syncthreads();  // the table's LDS is reused by the stages below
   } else {
     const int mtn = g.M / BM, ntn = g.N / BN;
     const int L = xcd_chunked(blockIdx.x, g.E * mtn * ntn);
@@ -106,186 +124,253 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmArgs g) {
     nk = (seglen + BK - 1) / BK;
   }
 
-  // ---- per-thread load state
-  // k-contiguous tiles: rows (tid>>3) + 32*i, 16-byte chunk (tid&7)
-  // mn-contiguous tiles: k-rows (tid>>4) + 16*i, 16-byte chunk (tid&15)
-  const uint16_t *a_row[4];
-  bool a_ok[4];
-  const uint16_t *b_row[4];
+  // ---- per-thread load state (grouped-M): fixed row pointers
+  //  k-contiguous tile of R rows: rows (tid>>3) + 32*i, 16-byte chunk (tid&7)
+  //  mn-contiguous tile of C cols: k-rows (tid / (C/8)) + (256/(C/8))*i, chunk tid % (C/8)
+  const uint16_t *a_row[A_LD];
+  const uint16_t *b_ptr[B_LD];
   if constexpr (MODE == GROUPED_M) {
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < A_LD; i++) {
+      // rows past the segment re-read the tile's first row: their accumulator rows
+      // are never stored, so they need no zeroing
       const int r = (tid >> 3) + 32 * i;
-      a_ok[i] = r < rows;
-      const int s = row0 + r;
-      const int64_t gr = a_ok[i] ? (g.a_rows ? g.a_rows[s] : s) : 0;
+      const int s = row0 + (r < rows ? r : 0);
+      const int64_t gr = g.a_rows ? g.a_rows[s] : s;
       a_row[i] = A + gr * g.lda + (tid & 7) * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < B_LD; i++) {
       if constexpr (B_KC) {
         const int64_t n = (int64_t)nt * BN + (tid >> 3) + 32 * i;
-        b_row[i] = B + (int64_t)e * g.b_es + n * g.ldb + (tid & 7) * 8;
+        b_ptr[i] = B + (int64_t)e * g.b_es + n * g.ldb + (tid & 7) * 8;
       } else {
-        b_row[i] = B + (int64_t)e * g.b_es + (int64_t)((tid >> 4) + 16 * i) * g.ldb +
-                   (int64_t)nt * BN + (tid & 15) * 8;
+        constexpr int CPR = BN / 8;  // chunks per k-row
+        const int kr = tid / CPR + (NT / CPR) * i;
+        b_ptr[i] = B + (int64_t)e * g.b_es + (int64_t)kr * g.ldb + (int64_t)nt * BN +
+                   (tid % CPR) * 8;
       }
     }
   }
 
-  uint4 ra[4], rb[4];
-  auto load = [&](int k0) {
-    if constexpr (MODE == GROUPED_M) {
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        ra[i] = a_ok[i] ? *(const uint4 *)(a_row[i] + k0) : make_uint4(0, 0, 0, 0);
-        if constexpr (B_KC)
-          rb[i] = *(const uint4 *)(b_row[i] + k0);
-        else
-          rb[i] = *(const uint4 *)(b_row[i] + (int64_t)k0 * g.ldb);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int kk = k0 + (tid >> 4) + 16 * i;
-        if (kk < seglen) {
-          const int s = seg0 + kk;
-          const int64_t ga = g.a_rows ? g.a_rows[s] : s;
-          const int64_t gb = g.b_rows ? g.b_rows[s] : s;
-          ra[i] = *(const uint4 *)(A + ga * g.lda + (int64_t)mt * BM + (tid & 15) * 8);
-          rb[i] = *(const uint4 *)(B + gb * g.ldb + (int64_t)nt * BN + (tid & 15) * 8);
-        } else {
-          ra[i] = make_uint4(0, 0, 0, 0);
-          rb[i] = make_uint4(0, 0, 0, 0);
-        }
-      }
-    }
-  };
-  auto store = [&](int stage) {
-    uint16_t *As = smem + stage * 2 * TILE;
-    uint16_t *Bs = As + TILE;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      if constexpr (A_KC)
-        *(uint4 *)(As + ((tid >> 3) + 32 * i) * LDK + (tid & 7) * 8) = ra[i];
-      else
-        *(uint4 *)(As + ((tid >> 4) + 16 * i) * LDC + (tid & 15) * 8) = ra[i];
-      if constexpr (B_KC) {
-        *(uint4 *)(Bs + ((tid >> 3) + 32 * i) * LDK + (tid & 7) * 8) = rb[i];
-      } else if constexpr (EPI == EPI_SWIGLU) {
-        // interleaved (gate_j, up_j) columns -> gates of the wave's 32 pairs, then ups
-        const int nc = tid & 15;
-        const int base = ((tid >> 4) + 16 * i) * LDC + (nc >> 3) * 64 + 4 * (nc & 7);
-        const uint4 v = rb[i];
-        uint2 gate, up;
-        gate.x = (v.x & 0xffffu) | (v.y << 16);
-        gate.y = (v.z & 0xffffu) | (v.w << 16);
-        up.x = (v.x >> 16) | (v.y & 0xffff0000u);
-        up.y = (v.z >> 16) | (v.w & 0xffff0000u);
-        *(uint2 *)(Bs + base) = gate;
-        *(uint2 *)(Bs + base + 32) = up;
-      } else {
-        *(uint4 *)(Bs + ((tid >> 4) + 16 * i) * LDC + (tid & 15) * 8) = rb[i];
-      }
-    }
-  };
+  // Register sets and LDS stages are handled by macros so every array index is a
+  // compile-time constant in this scope (the arrays then live in VGPRs).
+  //  LOAD(ra, rb, k0): global -> registers for the tile at reduction offset k0
+  //  STORE(ra, rb, st): registers -> LDS stage st
+  //  COMPUTE(st): the MFMAs over LDS stage st
+#define MOE_LOAD(ra, rb, k0_)                                                              \
+  do {                                                                                     \
+    const int k0 = (k0_);                                                                  \
+    if constexpr (MODE == GROUPED_M) {                                                     \
+      _Pragma("unroll") for (int i = 0; i < A_LD; i++) ra[i] =                             \
+          *(const u32x4 *)(a_row[i] + k0);                                                 \
+      _Pragma("unroll") for (int i = 0; i < B_LD; i++) {                                   \
+        if constexpr (B_KC)                                                                \
+          rb[i] = *(const u32x4 *)(b_ptr[i] + k0);                                         \
+        else                                                                               \
+          rb[i] = *(const u32x4 *)(b_ptr[i] + (int64_t)k0 * g.ldb);                        \
+      }                                                                                    \
+    } else {                                                                               \
+      constexpr int CPA = BM / 8, CPB = BN / 8;                                            \
+      _Pragma("unroll") for (int i = 0; i < A_LD; i++) {                                   \
+        const int kk = k0 + tid / CPA + (NT / CPA) * i;                                    \
+        if (kk < seglen) {                                                                 \
+          const int s_ = seg0 + kk;                                                        \
+          const int64_t ga = g.a_rows ? g.a_rows[s_] : s_;                                 \
+          ra[i] = *(const u32x4 *)(A + ga * g.lda + (int64_t)mt * BM + (tid % CPA) * 8);   \
+        } else {                                                                           \
+          ra[i] = u32x4{0, 0, 0, 0};                                                  \
+        }                                                                                  \
+      }                                                                                    \
+      _Pragma("unroll") for (int i = 0; i < B_LD; i++) {                                   \
+        const int kk = k0 + tid / CPB + (NT / CPB) * i;                                    \
+        if (kk < seglen) {                                                                 \
+          const int s_ = seg0 + kk;                                                        \
+          const int64_t gb = g.b_rows ? g.b_rows[s_] : s_;                                 \
+          rb[i] = *(const u32x4 *)(B + gb * g.ldb + (int64_t)nt * BN + (tid % CPB) * 8);   \
+        } else {                                                                           \
+          rb[i] = u32x4{0, 0, 0, 0};                                                  \
+        }                                                                                  \
+      }                                                                                    \
+    }                                                                                      \
+  } while (0)
 
-  f32x16 acc[2][2];
+#define MOE_STORE(ra, rb, st)                                                              \
+  do {                                                                                     \
+    uint16_t *As_ = smem + (st) * STAGE;                                                   \
+    uint16_t *Bs_ = As_ + AS::elems;                                                       \
+    _Pragma("unroll") for (int i = 0; i < A_LD; i++) {                                     \
+      if constexpr (A_KC) {                                                                \
+        *(u32x4 *)(As_ + ((tid >> 3) + 32 * i) * LDK + (tid & 7) * 8) = ra[i];             \
+      } else {                                                                             \
+        constexpr int CPA = BM / 8;                                                        \
+        *(u32x4 *)(As_ + (tid / CPA + (NT / CPA) * i) * AS::ld + (tid % CPA) * 8) = ra[i]; \
+      }                                                                                    \
+    }                                                                                      \
+    _Pragma("unroll") for (int i = 0; i < B_LD; i++) {                                     \
+      if constexpr (B_KC) {                                                                \
+        *(u32x4 *)(Bs_ + ((tid >> 3) + 32 * i) * LDK + (tid & 7) * 8) = rb[i];             \
+      } else {                                                                             \
+        constexpr int CPB = BN / 8;                                                        \
+        const int kr = tid / CPB + (NT / CPB) * i;                                         \
+        const int nc = tid % CPB;                                                          \
+        if constexpr (EPI == EPI_SWIGLU) {                                                 \
+          /* interleaved (gate_j, up_j) columns -> per wave: its gates, then its ups */    \
+          const int half = (nc * 8) / WN;                                                  \
+          const int p0 = 4 * (nc % (WN / 8));                                              \
+          const int base = kr * BS::ld + half * WN + p0;                                   \
+          const u32x4 v = rb[i];                                                           \
+          u32x2 gate, up;                                                                  \
+          gate.x = (v.x & 0xffffu) | (v.y << 16);                                          \
+          gate.y = (v.z & 0xffffu) | (v.w << 16);                                          \
+          up.x = (v.x >> 16) | (v.y & 0xffff0000u);                                        \
+          up.y = (v.z >> 16) | (v.w & 0xffff0000u);                                        \
+          *(u32x2 *)(Bs_ + base) = gate;                                                   \
+          *(u32x2 *)(Bs_ + base + WN / 2) = up;                                            \
+        } else {                                                                           \
+          *(u32x4 *)(Bs_ + kr * BS::ld + nc * 8) = rb[i];                                  \
+        }                                                                                  \
+      }                                                                                    \
+    }                                                                                      \
+  } while (0)
+
+#define MOE_COMPUTE(st)                                                                    \
+  do {                                                                                     \
+    const uint16_t *As_ = smem + (st) * STAGE;                                             \
+    const uint16_t *Bs_ = As_ + AS::elems;                                                 \
+    _Pragma("unroll") for (int ks = 0; ks < BK / 16; ks++) {                               \
+      bf16x8 af[TM], bfr[TN];                                                              \
+      _Pragma("unroll") for (int mi = 0; mi < TM; mi++) {                                  \
+        if constexpr (A_KC)                                                                \
+          af[mi] = frag_kc(As_, wm * WM + mi * 32 + (lane & 31), ks * 16 + (lane >> 5) * 8); \
+        else                                                                               \
+          af[mi] = frag_mn<AS::ld>(As_, ks * 16, wm * WM + mi * 32, lane);                 \
+      }                                                                                    \
+      _Pragma("unroll") for (int ni = 0; ni < TN; ni++) {                                  \
+        if constexpr (B_KC)                                                                \
+          bfr[ni] = frag_kc(Bs_, wn * WN + ni * 32 + (lane & 31), ks * 16 + (lane >> 5) * 8); \
+        else                                                                               \
+          bfr[ni] = frag_mn<BS::ld>(Bs_, ks * 16, wn * WN + ni * 32, lane);                \
+      }                                                                                    \
+      _Pragma("unroll") for (int mi = 0; mi < TM; mi++)                                    \
+        _Pragma("unroll") for (int ni = 0; ni < TN; ni++) acc[mi][ni] =                    \
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0); \
+    }                                                                                      \
+  } while (0)
+
+  f32x16 acc[TM][TN];
 #pragma unroll
-  for (int mi = 0; mi < 2; mi++)
+  for (int mi = 0; mi < TM; mi++)
 #pragma unroll
-    for (int ni = 0; ni < 2; ni++)
+    for (int ni = 0; ni < TN; ni++)
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[mi][ni][r] = 0.0f;
 
-  if (nk > 0) {
-    load(0);
-    store(0);
-  }
+  // Two LDS stages and two register sets: the tile stored into a stage was loaded
+  // from memory two tiles earlier, so each global load has about two tiles of MFMA
+  // work to arrive.
+  u32x4 ra0[A_LD], rb0[B_LD], ra1[A_LD], rb1[B_LD];
+  if (nk > 0) MOE_LOAD(ra0, rb0, 0);
+  if (nk > 1) MOE_LOAD(ra1, rb1, BK);
+  if (nk > 0) MOE_STORE(ra0, rb0, 0);
+  if (nk > 2) MOE_LOAD(ra0, rb0, 2 * BK);
   __syncthreads();
-  for (int kt = 0; kt < nk; kt++) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load((kt + 1) * BK);
-    const uint16_t *As = smem + cur * 2 * TILE;
-    const uint16_t *Bs = As + TILE;
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ks++) {
-      bf16x8 af[2], bfr[2];
-#pragma unroll
-      for (int mi = 0; mi < 2; mi++) {
-        if constexpr (A_KC)
-          af[mi] = frag_kc(As, wm * 64 + mi * 32 + (lane & 31), ks * 16 + (lane >> 5) * 8);
-        else
-          af[mi] = frag_mn(As, ks * 16, wm * 64 + mi * 32, lane);
-      }
-#pragma unroll
-      for (int ni = 0; ni < 2; ni++) {
-        if constexpr (B_KC)
-          bfr[ni] = frag_kc(Bs, wn * 64 + ni * 32 + (lane & 31), ks * 16 + (lane >> 5) * 8);
-        else
-          bfr[ni] = frag_mn(Bs, ks * 16, wn * 64 + ni * 32, lane);
-      }
-#pragma unroll
-      for (int mi = 0; mi < 2; mi++)
-#pragma unroll
-        for (int ni = 0; ni < 2; ni++)
-          acc[mi][ni] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+  for (int kt = 0; kt < nk; kt += 2) {
+    MOE_COMPUTE(0);  // tile kt
+    if (kt + 1 < nk) {
+      MOE_STORE(ra1, rb1, 1);
+      if (kt + 3 < nk) MOE_LOAD(ra1, rb1, (kt + 3) * BK);
     }
-    if (kt + 1 < nk) store(cur ^ 1);
     __syncthreads();
+    if (kt + 1 < nk) {
+      MOE_COMPUTE(1);  // tile kt+1
+      if (kt + 2 < nk) {
+        MOE_STORE(ra0, rb0, 0);
+        if (kt + 4 < nk) MOE_LOAD(ra0, rb0, (kt + 4) * BK);
+      }
+      __syncthreads();
+    }
   }
+#undef MOE_LOAD
+#undef MOE_STORE
+#undef MOE_COMPUTE
 
   // ---- epilogues. Accumulator (mi, ni, r) of lane l holds tile row
-  // wm*64 + mi*32 + (r/4)*8 + (l/32)*4 + r%4 and column wn*64 + ni*32 + l%32.
+  // wm*WM + mi*32 + (r/4)*8 + (l/32)*4 + r%4 and column wn*WN + ni*32 + l%32.
   const int col_l = lane & 31;
   if constexpr (EPI == EPI_STORE) {
-    uint16_t *C = (uint16_t *)g.C;
+    // bf16 tile -> LDS [BM][BN+8] (adjacent lanes swap one value so each writes a
+    // column pair), then whole rows -> memory in 16-byte chunks
+    uint16_t *Cs = smem;
+    const bool odd = lane & 1;
 #pragma unroll
-    for (int mi = 0; mi < 2; mi++)
+    for (int mi = 0; mi < TM; mi++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int row = wm * 64 + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        int64_t off;
-        if constexpr (MODE == GROUPED_M) {
-          if (row >= rows) continue;
-          off = (int64_t)(row0 + row) * g.ldc;
-        } else {
-          off = (int64_t)e * g.c_es + (int64_t)(mt * BM + row) * g.ldc;
+      for (int ni = 0; ni < TN; ni++)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          // even lane keeps row r and receives (row r, col+1); odd lane keeps row r+1
+          const float send = odd ? acc[mi][ni][r] : acc[mi][ni][r + 1];
+          const float recv = __shfl_xor(send, 1, kWave);
+          const int rr = odd ? r + 1 : r;
+          const int row = wm * WM + mi * 32 + (rr >> 2) * 8 + (lane >> 5) * 4 + (rr & 3);
+          const int col = wn * WN + ni * 32 + (col_l & ~1);
+          const uint32_t v = odd ? pack_bf16x2(recv, acc[mi][ni][r + 1])
+                                 : pack_bf16x2(acc[mi][ni][r], recv);
+          *(uint32_t *)(Cs + row * CLD + col) = v;
         }
+    __syncthreads();
+    uint16_t *C = (uint16_t *)g.C;
+    constexpr int CPR = BN / 8;
 #pragma unroll
-        for (int ni = 0; ni < 2; ni++)
-          C[off + (int64_t)nt * BN + wn * 64 + ni * 32 + col_l] = f32_to_bf16(acc[mi][ni][r]);
+    for (int i = 0; i < BM * CPR / NT; i++) {
+      const int c = tid + NT * i;
+      const int row = c / CPR, ch = c % CPR;
+      int64_t off;
+      if constexpr (MODE == GROUPED_M) {
+        if (row >= rows) continue;
+        off = (int64_t)(row0 + row) * g.ldc;
+      } else {
+        off = (int64_t)e * g.c_es + (int64_t)(mt * BM + row) * g.ldc;
       }
+      *(u32x4 *)(C + off + (int64_t)nt * BN + ch * 8) = *(const u32x4 *)(Cs + row * CLD + ch * 8);
+    }
   } else if constexpr (EPI == EPI_SWIGLU) {
     uint16_t *Hs = (uint16_t *)g.C;  // may be null (inference)
     uint16_t *Aout = (uint16_t *)g.C2;
-    const int pair = nt * (BN / 2) + wn * 32 + col_l;
 #pragma unroll
-    for (int mi = 0; mi < 2; mi++)
+    for (int mi = 0; mi < TM; mi++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int row = wm * 64 + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        if (row >= rows) continue;
-        const int64_t s = row0 + row;
-        const float gt = acc[mi][0][r], up = acc[mi][1][r];
-        if (Hs) *(uint32_t *)(Hs + s * g.ldc + 2 * pair) = pack_bf16x2(gt, up);
-        Aout[s * g.ldc2 + pair] = f32_to_bf16(silu_f(gt) * up);
+      for (int np = 0; np < TN / 2; np++) {
+        const int pair = nt * (BN / 2) + wn * (WN / 2) + np * 32 + col_l;
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const int row = wm * WM + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          if (row >= rows) continue;
+          const int64_t s = row0 + row;
+          const float gt = acc[mi][np][r], up = acc[mi][np + TN / 2][r];
+          if (Hs) *(uint32_t *)(Hs + s * g.ldc + 2 * pair) = pack_bf16x2(gt, up);
+          Aout[s * g.ldc2 + pair] = f32_to_bf16(silu_f(gt) * up);
+        }
       }
   } else {  // EPI_DSWIGLU: acc = da_u = dout_g W_down^T for pair columns j
     uint16_t *dH = (uint16_t *)g.C;
     uint16_t *AW = (uint16_t *)g.C2;
     const uint16_t *Hs = (const uint16_t *)g.Hs;
-    float *red = (float *)smem;  // [2][128] row partials of the two column waves
+    float *red = (float *)smem;  // [2][BM] row partials of the two column waves (the
+                                 // loop's final barrier has released the stages)
 #pragma unroll
-    for (int mi = 0; mi < 2; mi++)
+    for (int mi = 0; mi < TM; mi++)
 #pragma unroll
       for (int r = 0; r < 16; r++) {
-        const int row = wm * 64 + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const int row = wm * WM + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
         float part = 0.0f;
         if (row < rows) {
           const int64_t s = row0 + row;
           const float wq = g.scores[g.s_scatter[s]];
 #pragma unroll
-          for (int ni = 0; ni < 2; ni++) {
-            const int j = nt * BN + wn * 64 + ni * 32 + col_l;
+          for (int ni = 0; ni < TN; ni++) {
+            const int j = nt * BN + wn * WN + ni * 32 + col_l;
             const uint32_t hv = *(const uint32_t *)(Hs + s * g.ldh + 2 * j);
             const float gt = bf16_to_f32((uint16_t)(hv & 0xffffu));
             const float up = bf16_to_f32((uint16_t)(hv >> 16));
@@ -302,20 +387,65 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmArgs g) {
         }
 #pragma unroll
         for (int o = 16; o >= 1; o >>= 1) part += __shfl_xor(part, o, kWave);
-        if (col_l == 0) red[wn * 128 + row] = part;
+        if (col_l == 0) red[wn * BM + row] = part;
       }
     __syncthreads();
-    if (tid < BM && tid < rows)
-      g.partial[(int64_t)(row0 + tid) * g.n_ntiles + nt] = red[tid] + red[128 + tid];
+    for (int r = tid; r < rows; r += NT)
+      g.partial[(int64_t)(row0 + r) * g.n_ntiles + nt] = red[r] + red[BM + r];
   }
+}
+
+template <int MODE, bool A_KC, bool B_KC, int EPI>
+hipError_t launch_tiles(int bm, int bn, int grid, const GemmArgs &g, hipStream_t st) {
+  if (bm == 128 && bn == 128)
+    hipLaunchKernelGGL((gemm_bf16_kernel<MODE, A_KC, B_KC, EPI, 128, 128>), dim3(grid), dim3(NT),
+                       0, st, g);
+  else if (bm == 128 && bn == 256)
+    hipLaunchKernelGGL((gemm_bf16_kernel<MODE, A_KC, B_KC, EPI, 128, 256>), dim3(grid), dim3(NT),
+                       0, st, g);
+  else if (bm == 256 && bn == 128)
+    hipLaunchKernelGGL((gemm_bf16_kernel<MODE, A_KC, B_KC, EPI, 256, 128>), dim3(grid), dim3(NT),
+                       0, st, g);
+  else if (bm == 256 && bn == 256)
+    hipLaunchKernelGGL((gemm_bf16_kernel<MODE, A_KC, B_KC, EPI, 256, 256>), dim3(grid), dim3(NT),
+                       0, st, g);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace
 
+// Tile shape per GEMM: the larger tiles where the fixed dimensions allow them.
+#ifndef MOE_TILE_GM_BM
+#define MOE_TILE_GM_BM 128
+#endif
+#ifndef MOE_TILE_GM_BN
+#define MOE_TILE_GM_BN 128
+#endif
+#ifndef MOE_TILE_VK_BM
+#define MOE_TILE_VK_BM 128
+#endif
+#ifndef MOE_TILE_VK_BN
+#define MOE_TILE_VK_BN 128
+#endif
+
+void gemm_tile(GemmKind kind, const GemmArgs &g, int *bm, int *bn) {
+  if (kind == kWeightGrad) {
+    *bm = (g.M % MOE_TILE_VK_BM == 0) ? MOE_TILE_VK_BM : 128;
+    *bn = (g.N % MOE_TILE_VK_BN == 0) ? MOE_TILE_VK_BN : 128;
+  } else {
+    *bm = MOE_TILE_GM_BM;
+    *bn = (g.N % MOE_TILE_GM_BN == 0) ? MOE_TILE_GM_BN : 128;
+  }
+}
+
 int gemm_grid(GemmKind kind, const GemmArgs &g) {
-  if (kind == kWeightGrad) return g.E * (g.M / BM) * (g.N / BN);
-  const int64_t mt = ((int64_t)g.cap + (int64_t)g.E * (BM - 1)) / BM;
-  const int64_t grid = mt * (g.N / BN);
+  int bm, bn;
+  gemm_tile(kind, g, &bm, &bn);
+  if (kind == kWeightGrad) return g.E * (g.M / bm) * (g.N / bn);
+  const int64_t mt = ((int64_t)g.cap + (int64_t)g.E * (bm - 1)) / bm;
+  const int64_t grid = mt * (g.N / bn);
   return grid > 0x7fffffff ? -1 : (int)grid;
 }
 
@@ -323,31 +453,22 @@ hipError_t launch_gemm_bf16(GemmKind kind, const GemmArgs &g, hipStream_t st) {
   const int grid = gemm_grid(kind, g);
   if (grid < 0) return hipErrorInvalidValue;
   if (grid == 0) return hipSuccess;
+  int bm, bn;
+  gemm_tile(kind, g, &bm, &bn);
   switch (kind) {
     case kUpSwiGLU:
-      hipLaunchKernelGGL((gemm_bf16_kernel<GROUPED_M, true, false, EPI_SWIGLU>), dim3(grid),
-                         dim3(NT), 0, st, g);
-      break;
+      return launch_tiles<GROUPED_M, true, false, EPI_SWIGLU>(bm, bn, grid, g, st);
     case kDown:
-      hipLaunchKernelGGL((gemm_bf16_kernel<GROUPED_M, true, false, EPI_STORE>), dim3(grid),
-                         dim3(NT), 0, st, g);
-      break;
+      return launch_tiles<GROUPED_M, true, false, EPI_STORE>(bm, bn, grid, g, st);
     case kDownBwd:
-      hipLaunchKernelGGL((gemm_bf16_kernel<GROUPED_M, true, true, EPI_DSWIGLU>), dim3(grid),
-                         dim3(NT), 0, st, g);
-      break;
+      return launch_tiles<GROUPED_M, true, true, EPI_DSWIGLU>(bm, bn, grid, g, st);
     case kUpBwd:
-      hipLaunchKernelGGL((gemm_bf16_kernel<GROUPED_M, true, true, EPI_STORE>), dim3(grid),
-                         dim3(NT), 0, st, g);
-      break;
+      return launch_tiles<GROUPED_M, true, true, EPI_STORE>(bm, bn, grid, g, st);
     case kWeightGrad:
-      hipLaunchKernelGGL((gemm_bf16_kernel<VARLEN_K, false, false, EPI_STORE>), dim3(grid),
-                         dim3(NT), 0, st, g);
-      break;
+      return launch_tiles<VARLEN_K, false, false, EPI_STORE>(bm, bn, grid, g, st);
     default:
       return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -182,8 +182,15 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(GemmArgs g) {
 
 }  // namespace
 
+int gemm_grid_f32(GemmKind kind, const GemmArgs &g) {
+  if (kind == kWeightGrad) return g.E * (g.M / BM) * (g.N / BN);
+  const int64_t mt = ((int64_t)g.cap + (int64_t)g.E * (BM - 1)) / BM;
+  const int64_t grid = mt * (g.N / BN);
+  return grid > 0x7fffffff ? -1 : (int)grid;
+}
+
 hipError_t launch_gemm_f32(GemmKind kind, const GemmArgs &g, hipStream_t st) {
-  const int grid = gemm_grid(kind, g);
+  const int grid = gemm_grid_f32(kind, g);
   if (grid < 0) return hipErrorInvalidValue;
   if (grid == 0) return hipSuccess;
   switch (kind) {
