@@ -155,10 +155,24 @@ __global__ __launch_bounds__(NT, (BM * BN <= 128 * 128) ? 2 : 1) void gemm_bf16_
 
   // Register sets and LDS stages are handled by macros so every array index is a
   // compile-time constant in this scope (the arrays then live in VGPRs).
-  //  LOAD(ra, rb, k0): global -> registers for the tile at reduction offset k0
+  //  LOAD(ra, rb, ia, ib, k0): global -> registers for the tile at reduction offset k0
   //  STORE(ra, rb, st): registers -> LDS stage st
   //  COMPUTE(st): the MFMAs over LDS stage st
-#define MOE_LOAD(ra, rb, k0_)                                                              \
+  //  ROWS(ia, ib, k0): (varlen-K) memory rows of the tile at reduction offset k0
+#define MOE_ROWS(ia, ib, k0_)                                                              \
+  do {                                                                                     \
+    constexpr int CPA = BM / 8, CPB = BN / 8;                                              \
+    _Pragma("unroll") for (int i = 0; i < A_LD; i++) {                                     \
+      const int kk = (k0_) + tid / CPA + (NT / CPA) * i;                                   \
+      ia[i] = kk < seglen ? (g.a_rows ? g.a_rows[seg0 + kk] : seg0 + kk) : -1;             \
+    }                                                                                      \
+    _Pragma("unroll") for (int i = 0; i < B_LD; i++) {                                     \
+      const int kk = (k0_) + tid / CPB + (NT / CPB) * i;                                   \
+      ib[i] = kk < seglen ? (g.b_rows ? g.b_rows[seg0 + kk] : seg0 + kk) : -1;             \
+    }                                                                                      \
+  } while (0)
+
+#define MOE_LOAD(ra, rb, ia, ib, k0_)                                                      \
   do {                                                                                     \
     const int k0 = (k0_);                                                                  \
     if constexpr (MODE == GROUPED_M) {                                                     \
@@ -171,27 +185,19 @@ __global__ __launch_bounds__(NT, (BM * BN <= 128 * 128) ? 2 : 1) void gemm_bf16_
           rb[i] = *(const u32x4 *)(b_ptr[i] + (int64_t)k0 * g.ldb);                        \
       }                                                                                    \
     } else {                                                                               \
+      /* rows were looked up one load earlier (ia/ib); -1 = past the segment -> 0 */       \
       constexpr int CPA = BM / 8, CPB = BN / 8;                                            \
       _Pragma("unroll") for (int i = 0; i < A_LD; i++) {                                   \
-        const int kk = k0 + tid / CPA + (NT / CPA) * i;                                    \
-        if (kk < seglen) {                                                                 \
-          const int s_ = seg0 + kk;                                                        \
-          const int64_t ga = g.a_rows ? g.a_rows[s_] : s_;                                 \
-          ra[i] = *(const u32x4 *)(A + ga * g.lda + (int64_t)mt * BM + (tid % CPA) * 8);   \
-        } else {                                                                           \
-          ra[i] = u32x4{0, 0, 0, 0};                                                  \
-        }                                                                                  \
+        const int64_t r_ = ia[i] < 0 ? 0 : ia[i];                                          \
+        const u32x4 v_ = *(const u32x4 *)(A + r_ * g.lda + (int64_t)mt * BM + (tid % CPA) * 8); \
+        ra[i] = ia[i] < 0 ? u32x4{0, 0, 0, 0} : v_;                                        \
       }                                                                                    \
       _Pragma("unroll") for (int i = 0; i < B_LD; i++) {                                   \
-        const int kk = k0 + tid / CPB + (NT / CPB) * i;                                    \
-        if (kk < seglen) {                                                                 \
-          const int s_ = seg0 + kk;                                                        \
-          const int64_t gb = g.b_rows ? g.b_rows[s_] : s_;                                 \
-          rb[i] = *(const u32x4 *)(B + gb * g.ldb + (int64_t)nt * BN + (tid % CPB) * 8);   \
-        } else {                                                                           \
-          rb[i] = u32x4{0, 0, 0, 0};                                                  \
-        }                                                                                  \
+        const int64_t r_ = ib[i] < 0 ? 0 : ib[i];                                          \
+        const u32x4 v_ = *(const u32x4 *)(B + r_ * g.ldb + (int64_t)nt * BN + (tid % CPB) * 8); \
+        rb[i] = ib[i] < 0 ? u32x4{0, 0, 0, 0} : v_;                                        \
       }                                                                                    \
+      MOE_ROWS(ia, ib, k0 + 2 * BK);                                                       \
     }                                                                                      \
   } while (0)
 
@@ -270,28 +276,34 @@ __global__ __launch_bounds__(NT, (BM * BN <= 128 * 128) ? 2 : 1) void gemm_bf16_
   // from memory two tiles earlier, so each global load has about two tiles of MFMA
   // work to arrive.
   u32x4 ra0[A_LD], rb0[B_LD], ra1[A_LD], rb1[B_LD];
-  if (nk > 0) MOE_LOAD(ra0, rb0, 0);
-  if (nk > 1) MOE_LOAD(ra1, rb1, BK);
+  int ia0[A_LD], ib0[B_LD], ia1[A_LD], ib1[B_LD];  // varlen-K: rows of each set's next tile
+  if constexpr (MODE == VARLEN_K) {
+    MOE_ROWS(ia0, ib0, 0);
+    MOE_ROWS(ia1, ib1, BK);
+  }
+  if (nk > 0) MOE_LOAD(ra0, rb0, ia0, ib0, 0);
+  if (nk > 1) MOE_LOAD(ra1, rb1, ia1, ib1, BK);
   if (nk > 0) MOE_STORE(ra0, rb0, 0);
-  if (nk > 2) MOE_LOAD(ra0, rb0, 2 * BK);
+  if (nk > 2) MOE_LOAD(ra0, rb0, ia0, ib0, 2 * BK);
   __syncthreads();
   for (int kt = 0; kt < nk; kt += 2) {
     MOE_COMPUTE(0);  // tile kt
     if (kt + 1 < nk) {
       MOE_STORE(ra1, rb1, 1);
-      if (kt + 3 < nk) MOE_LOAD(ra1, rb1, (kt + 3) * BK);
+      if (kt + 3 < nk) MOE_LOAD(ra1, rb1, ia1, ib1, (kt + 3) * BK);
     }
     __syncthreads();
     if (kt + 1 < nk) {
       MOE_COMPUTE(1);  // tile kt+1
       if (kt + 2 < nk) {
         MOE_STORE(ra0, rb0, 0);
-        if (kt + 4 < nk) MOE_LOAD(ra0, rb0, (kt + 4) * BK);
+        if (kt + 4 < nk) MOE_LOAD(ra0, rb0, ia0, ib0, (kt + 4) * BK);
       }
       __syncthreads();
     }
   }
 #undef MOE_LOAD
+#undef MOE_ROWS
 #undef MOE_STORE
 #undef MOE_COMPUTE
 
@@ -354,41 +366,79 @@ __global__ __launch_bounds__(NT, (BM * BN <= 128 * 128) ? 2 : 1) void gemm_bf16_
         }
       }
   } else {  // EPI_DSWIGLU: acc = da_u = dout_g W_down^T for pair columns j
-    uint16_t *dH = (uint16_t *)g.C;
-    uint16_t *AW = (uint16_t *)g.C2;
-    const uint16_t *Hs = (const uint16_t *)g.Hs;
+    uint16_t *__restrict__ dH = (uint16_t *)g.C;
+    uint16_t *__restrict__ AW = (uint16_t *)g.C2;
+    const uint16_t *__restrict__ Hs = (const uint16_t *)g.Hs;
+    const float *__restrict__ scores = g.scores;
+    const int32_t *__restrict__ s_scatter = g.s_scatter;
     float *red = (float *)smem;  // [2][BM] row partials of the two column waves (the
                                  // loop's final barrier has released the stages)
 #pragma unroll
-    for (int mi = 0; mi < TM; mi++)
+    for (int mi = 0; mi < TM; mi++) {
+      // all loads of this row block first: router weights and saved (gate, up) pairs;
+      // rows past the segment read row 0 of the tile and are never stored
+      int64_t srow[16];
+      float wq[16];
+      uint32_t hv[TN][16];
 #pragma unroll
       for (int r = 0; r < 16; r++) {
         const int row = wm * WM + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        float part = 0.0f;
-        if (row < rows) {
-          const int64_t s = row0 + row;
-          const float wq = g.scores[g.s_scatter[s]];
+        srow[r] = row0 + (row < rows ? row : 0);
+      }
+      int qv[16];
 #pragma unroll
-          for (int ni = 0; ni < TN; ni++) {
-            const int j = nt * BN + wn * WN + ni * 32 + col_l;
-            const uint32_t hv = *(const uint32_t *)(Hs + s * g.ldh + 2 * j);
-            const float gt = bf16_to_f32((uint16_t)(hv & 0xffffu));
-            const float up = bf16_to_f32((uint16_t)(hv >> 16));
-            const float dau = acc[mi][ni][r];
-            const float sg = sigmoid_f(gt);
-            const float a = gt * sg * up;
-            part += dau * a;
-            const float da = wq * dau;
-            const float dg = da * up * sg * (1.0f + gt * (1.0f - sg));
-            const float du = da * gt * sg;
-            *(uint32_t *)(dH + s * g.ldc + 2 * j) = pack_bf16x2(dg, du);
-            AW[s * g.ldc2 + j] = f32_to_bf16(wq * a);
+      for (int r = 0; r < 16; r++) qv[r] = s_scatter[srow[r]];
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        wq[r] = scores[qv[r]];
+#pragma unroll
+        for (int ni = 0; ni < TN; ni++) {
+          const int j = nt * BN + wn * WN + ni * 32 + col_l;
+          hv[ni][r] = *(const uint32_t *)(Hs + srow[r] * g.ldh + 2 * j);
+        }
+      }
+      float part[16];
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int row = wm * WM + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const bool ok = row < rows;
+        part[r] = 0.0f;
+#pragma unroll
+        for (int ni = 0; ni < TN; ni++) {
+          const int j = nt * BN + wn * WN + ni * 32 + col_l;
+          const float gt = bf16_to_f32((uint16_t)(hv[ni][r] & 0xffffu));
+          const float up = bf16_to_f32((uint16_t)(hv[ni][r] >> 16));
+          const float dau = acc[mi][ni][r];
+          const float sg = sigmoid_f(gt);
+          const float a = gt * sg * up;
+          part[r] += dau * a;
+          const float da = wq[r] * dau;
+          const float dg = da * up * sg * (1.0f + gt * (1.0f - sg));
+          const float du = da * gt * sg;
+          if (ok) {
+            *(uint32_t *)(dH + srow[r] * g.ldc + 2 * j) = pack_bf16x2(dg, du);
+            AW[srow[r] * g.ldc2 + j] = f32_to_bf16(wq[r] * a);
           }
         }
-#pragma unroll
-        for (int o = 16; o >= 1; o >>= 1) part += __shfl_xor(part, o, kWave);
-        if (col_l == 0) red[wn * BM + row] = part;
+        if (!ok) part[r] = 0.0f;
       }
+      // butterfly over the 32 lanes of each half: after exchanging half of the
+      // values at each step, lane l holds the full row sum for r = (l%32)/2
+#pragma unroll
+      for (int n = 16, o = 16; n > 1; n >>= 1, o >>= 1) {
+        const bool upper = (lane & o) != 0;
+#pragma unroll
+        for (int i = 0; i < n / 2; i++) {
+          const float send = upper ? part[i] : part[i + n / 2];
+          const float keep = upper ? part[i + n / 2] : part[i];
+          part[i] = keep + __shfl_xor(send, o, kWave);
+        }
+      }
+      const float rsum = part[0] + __shfl_xor(part[0], 1, kWave);
+      const int rr = (lane & 31) >> 1;
+      const int row = wm * WM + mi * 32 + (rr >> 2) * 8 + (lane >> 5) * 4 + (rr & 3);
+      if ((lane & 1) == 0) red[wn * BM + row] = rsum;
+    }
     __syncthreads();
     for (int r = tid; r < rows; r += NT)
       g.partial[(int64_t)(row0 + r) * g.n_ntiles + nt] = red[r] + red[BM + r];
