@@ -244,8 +244,8 @@ moe_status moe_expert_backward(const moe_metadata *meta, const int32_t *topk_idx
   g.s_scatter = meta->s_scatter_idx;
   g.partial = partial;
   if (dt == MOE_BF16) {  // one dscore partial per column tile of this GEMM
-    int bm, bn;
-    gemm_tile(kDownBwd, g, &bm, &bn);
+    int bm, bn, bk;
+    gemm_tile(kDownBwd, g, &bm, &bn, &bk);
     g.n_ntiles = I / bn;
   } else {
     g.n_ntiles = I / kGemmBN;

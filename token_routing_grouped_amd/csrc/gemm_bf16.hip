@@ -34,23 +34,24 @@
 namespace moe {
 namespace {
 
-constexpr int BK = kGemmBK, NT = 256;
-constexpr int LDK = BK + 8;  // row stride of a reduction-contiguous tile [rows][BK]
-constexpr int PADC = 32;     // extra columns of an M/N-contiguous tile [BK][cols]
+constexpr int NT = 256;
+constexpr int PADK = 8;   // extra elements per row of a reduction-contiguous tile [rows][BK]
+constexpr int PADC = 32;  // extra columns of an M/N-contiguous tile [BK][cols]
 
 enum { GROUPED_M = 0, VARLEN_K = 1 };
 enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_DSWIGLU = 2 };
 
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 
-template <bool KC, int R>
-struct TileShape {  // elements of one LDS stage of an operand with R rows (M or N)
-  static constexpr int ld = KC ? LDK : R + PADC;
-  static constexpr int elems = KC ? R * LDK : BK * (R + PADC);
+template <bool KC, int R, int BK>
+struct TileShape {  // one LDS stage of an operand with R rows (M or N) and BK reduction
+  static constexpr int ld = KC ? BK + PADK : R + PADC;
+  static constexpr int elems = KC ? R * (BK + PADK) : BK * (R + PADC);
 };
 
+template <int LD>
 __device__ __forceinline__ bf16x8 frag_kc(const uint16_t *tile, int r, int kk) {
-  return __builtin_bit_cast(bf16x8, *(const u32x4 *)(tile + r * LDK + kk));
+  return __builtin_bit_cast(bf16x8, *(const u32x4 *)(tile + r * LD + kk));
 }
 
 // Operand of v_mfma_f32_32x32x16_bf16 from a [k][col] tile with row stride ld:
@@ -68,18 +69,20 @@ __device__ __forceinline__ bf16x8 frag_mn(const uint16_t *tile, int kbase, int c
   return __builtin_bit_cast(bf16x8, v);
 }
 
-template <int MODE, bool A_KC, bool B_KC, int EPI, int BM, int BN>
-__global__ __launch_bounds__(NT, (BM * BN <= 128 * 128) ? 2 : 1) void gemm_bf16_kernel(GemmArgs g) {
+template <int MODE, bool A_KC, bool B_KC, int EPI, int BM, int BN, int BK>
+__global__ __launch_bounds__(NT, (BM * BN > 128 * 128) ? 1 : (BK == 32 ? 3 : 2))
+void gemm_bf16_kernel(GemmArgs g) {
   constexpr int TM = BM / 64, TN = BN / 64;  // 32x32 sub-tiles per wave
   constexpr int WM = BM / 2, WN = BN / 2;    // wave tile
-  using AS = TileShape<A_KC, BM>;
-  using BS = TileShape<B_KC, BN>;
+  using AS = TileShape<A_KC, BM, BK>;
+  using BS = TileShape<B_KC, BN, BK>;
+  constexpr int CPK = BK / 8;  // 16-byte chunks per row of a reduction-contiguous tile
   constexpr int STAGE = AS::elems + BS::elems;
   constexpr int CLD = BN + 8;  // C staging row stride (elements)
   static_assert(BM * CLD <= 2 * STAGE, "C staging fits in the stage buffers");
-  static_assert(2 * STAGE * 2 >= (MOE_MAX_EXPERTS + 2) * 4, "tile table fits");
-  constexpr int A_LD = BM / 32;  // 16-byte chunks per thread per stage
-  constexpr int B_LD = BN / 32;
+  static_assert(2 * STAGE * 2 >= (2 * MOE_MAX_EXPERTS + 2) * 4, "tile tables fit");
+  constexpr int A_LD = BM * BK / (8 * NT);  // 16-byte chunks per thread per stage
+  constexpr int B_LD = BN * BK / (8 * NT);
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
   int *s_pref = (int *)smem;  // expert tile table, used before the first stage is written
 
@@ -113,19 +116,44 @@ __global__ __launch_bounds__(NT, (BM * BN <= 128 * 128) ? 2 : 1) void gemm_bf16_
     nk = g.K / BK;
     __syncthreads();  // the table's LDS is reused by the stages below
   } else {
-    const int mtn = g.M / BM, ntn = g.N / BN;
-    const int L = xcd_chunked(blockIdx.x, g.E * mtn * ntn);
-    e = L / (mtn * ntn);
-    const int r = L - e * (mtn * ntn);
-    mt = r / ntn;
-    nt = r - mt * ntn;
+    // Work per tile is the expert's row count, which can be very skewed. Experts are
+    // taken largest first, and every XCD gets one contiguous eighth of each expert's
+    // tiles: balanced across XCDs, and an XCD's tiles of one expert share rows in L2.
+    int *s_freq = (int *)smem;
+    int *s_order = s_freq + g.E;
+    for (int i = tid; i < g.E; i += NT) s_freq[i] = g.foff[i + 1] - g.foff[i];
+    __syncthreads();
+    for (int i = tid; i < g.E; i += NT) {
+      const int f = s_freq[i];
+      int rank = 0;
+      for (int j = 0; j < g.E; j++) {
+        const int fj = s_freq[j];
+        rank += (fj > f) || (fj == f && j < i);
+      }
+      s_order[rank] = i;
+    }
+    __syncthreads();
+    const int mtn = g.M / BM, ntn = g.N / BN, tpe = mtn * ntn;
+    int rank, tile;
+    if (tpe % kNumXcd == 0) {
+      const int c = tpe / kNumXcd, x = blockIdx.x % kNumXcd, i = blockIdx.x / kNumXcd;
+      rank = i / c;
+      tile = x * c + (i - rank * c);
+    } else {
+      rank = blockIdx.x / tpe;
+      tile = blockIdx.x - rank * tpe;
+    }
+    e = s_order[rank];
+    mt = tile / ntn;
+    nt = tile - mt * ntn;
     seg0 = g.foff[e];
     seglen = P > g.cap ? 0 : g.foff[e + 1] - seg0;
     nk = (seglen + BK - 1) / BK;
+    __syncthreads();  // the order table's LDS is reused by the stages below
   }
 
   // ---- per-thread load state (grouped-M): fixed row pointers
-  //  k-contiguous tile of R rows: rows (tid>>3) + 32*i, 16-byte chunk (tid&7)
+  //  k-contiguous tile of R rows: rows tid/CPK + (NT/CPK)*i, 16-byte chunk tid%CPK
   //  mn-contiguous tile of C cols: k-rows (tid / (C/8)) + (256/(C/8))*i, chunk tid % (C/8)
   const uint16_t *a_row[A_LD];
   const uint16_t *b_ptr[B_LD];
@@ -134,16 +162,16 @@ __global__ __launch_bounds__(NT, (BM * BN <= 128 * 128) ? 2 : 1) void gemm_bf16_
     for (int i = 0; i < A_LD; i++) {
       // rows past the segment re-read the tile's first row: their accumulator rows
       // are never stored, so they need no zeroing
-      const int r = (tid >> 3) + 32 * i;
+      const int r = tid / CPK + (NT / CPK) * i;
       const int s = row0 + (r < rows ? r : 0);
       const int64_t gr = g.a_rows ? g.a_rows[s] : s;
-      a_row[i] = A + gr * g.lda + (tid & 7) * 8;
+      a_row[i] = A + gr * g.lda + (tid % CPK) * 8;
     }
 #pragma unroll
     for (int i = 0; i < B_LD; i++) {
       if constexpr (B_KC) {
-        const int64_t n = (int64_t)nt * BN + (tid >> 3) + 32 * i;
-        b_ptr[i] = B + (int64_t)e * g.b_es + n * g.ldb + (tid & 7) * 8;
+        const int64_t n = (int64_t)nt * BN + tid / CPK + (NT / CPK) * i;
+        b_ptr[i] = B + (int64_t)e * g.b_es + n * g.ldb + (tid % CPK) * 8;
       } else {
         constexpr int CPR = BN / 8;  // chunks per k-row
         const int kr = tid / CPR + (NT / CPR) * i;
@@ -207,7 +235,7 @@ __global__ __launch_bounds__(NT, (BM * BN <= 128 * 128) ? 2 : 1) void gemm_bf16_
     uint16_t *Bs_ = As_ + AS::elems;                                                       \
     _Pragma("unroll") for (int i = 0; i < A_LD; i++) {                                     \
       if constexpr (A_KC) {                                                                \
-        *(u32x4 *)(As_ + ((tid >> 3) + 32 * i) * LDK + (tid & 7) * 8) = ra[i];             \
+        *(u32x4 *)(As_ + (tid / CPK + (NT / CPK) * i) * AS::ld + (tid % CPK) * 8) = ra[i]; \
       } else {                                                                             \
         constexpr int CPA = BM / 8;                                                        \
         *(u32x4 *)(As_ + (tid / CPA + (NT / CPA) * i) * AS::ld + (tid % CPA) * 8) = ra[i]; \
@@ -215,7 +243,7 @@ __global__ __launch_bounds__(NT, (BM * BN <= 128 * 128) ? 2 : 1) void gemm_bf16_
     }                                                                                      \
     _Pragma("unroll") for (int i = 0; i < B_LD; i++) {                                     \
       if constexpr (B_KC) {                                                                \
-        *(u32x4 *)(Bs_ + ((tid >> 3) + 32 * i) * LDK + (tid & 7) * 8) = rb[i];             \
+        *(u32x4 *)(Bs_ + (tid / CPK + (NT / CPK) * i) * BS::ld + (tid % CPK) * 8) = rb[i]; \
       } else {                                                                             \
         constexpr int CPB = BN / 8;                                                        \
         const int kr = tid / CPB + (NT / CPB) * i;                                         \
@@ -248,13 +276,13 @@ __global__ __launch_bounds__(NT, (BM * BN <= 128 * 128) ? 2 : 1) void gemm_bf16_
       bf16x8 af[TM], bfr[TN];                                                              \
       _Pragma("unroll") for (int mi = 0; mi < TM; mi++) {                                  \
         if constexpr (A_KC)                                                                \
-          af[mi] = frag_kc(As_, wm * WM + mi * 32 + (lane & 31), ks * 16 + (lane >> 5) * 8); \
+          af[mi] = frag_kc<AS::ld>(As_, wm * WM + mi * 32 + (lane & 31), ks * 16 + (lane >> 5) * 8); \
         else                                                                               \
           af[mi] = frag_mn<AS::ld>(As_, ks * 16, wm * WM + mi * 32, lane);                 \
       }                                                                                    \
       _Pragma("unroll") for (int ni = 0; ni < TN; ni++) {                                  \
         if constexpr (B_KC)                                                                \
-          bfr[ni] = frag_kc(Bs_, wn * WN + ni * 32 + (lane & 31), ks * 16 + (lane >> 5) * 8); \
+          bfr[ni] = frag_kc<BS::ld>(Bs_, wn * WN + ni * 32 + (lane & 31), ks * 16 + (lane >> 5) * 8); \
         else                                                                               \
           bfr[ni] = frag_mn<BS::ld>(Bs_, ks * 16, wn * WN + ni * 32, lane);                \
       }                                                                                    \
@@ -286,15 +314,29 @@ __global__ __launch_bounds__(NT, (BM * BN <= 128 * 128) ? 2 : 1) void gemm_bf16_
   if (nk > 0) MOE_STORE(ra0, rb0, 0);
   if (nk > 2) MOE_LOAD(ra0, rb0, ia0, ib0, 2 * BK);
   __syncthreads();
-  for (int kt = 0; kt < nk; kt += 2) {
+  int kt = 0;
+  // steady state, free of branches so the wait counters only hold back the set
+  // being stored (its loads are two tiles old), never the set loaded after it
+  for (; kt + 4 < nk; kt += 2) {
     MOE_COMPUTE(0);  // tile kt
+    MOE_STORE(ra1, rb1, 1);
+    MOE_LOAD(ra1, rb1, ia1, ib1, (kt + 3) * BK);
+    __syncthreads();
+    MOE_COMPUTE(1);  // tile kt+1
+    MOE_STORE(ra0, rb0, 0);
+    MOE_LOAD(ra0, rb0, ia0, ib0, (kt + 4) * BK);
+    __syncthreads();
+  }
+  // the last (at most four) tiles
+  for (; kt < nk; kt += 2) {
+    MOE_COMPUTE(0);
     if (kt + 1 < nk) {
       MOE_STORE(ra1, rb1, 1);
       if (kt + 3 < nk) MOE_LOAD(ra1, rb1, ia1, ib1, (kt + 3) * BK);
     }
     __syncthreads();
     if (kt + 1 < nk) {
-      MOE_COMPUTE(1);  // tile kt+1
+      MOE_COMPUTE(1);
       if (kt + 2 < nk) {
         MOE_STORE(ra0, rb0, 0);
         if (kt + 4 < nk) MOE_LOAD(ra0, rb0, ia0, ib0, (kt + 4) * BK);
@@ -446,22 +488,22 @@ __global__ __launch_bounds__(NT, (BM * BN <= 128 * 128) ? 2 : 1) void gemm_bf16_
 }
 
 template <int MODE, bool A_KC, bool B_KC, int EPI>
-hipError_t launch_tiles(int bm, int bn, int grid, const GemmArgs &g, hipStream_t st) {
-  if (bm == 128 && bn == 128)
-    hipLaunchKernelGGL((gemm_bf16_kernel<MODE, A_KC, B_KC, EPI, 128, 128>), dim3(grid), dim3(NT),
-                       0, st, g);
-  else if (bm == 128 && bn == 256)
-    hipLaunchKernelGGL((gemm_bf16_kernel<MODE, A_KC, B_KC, EPI, 128, 256>), dim3(grid), dim3(NT),
-                       0, st, g);
-  else if (bm == 256 && bn == 128)
-    hipLaunchKernelGGL((gemm_bf16_kernel<MODE, A_KC, B_KC, EPI, 256, 128>), dim3(grid), dim3(NT),
-                       0, st, g);
-  else if (bm == 256 && bn == 256)
-    hipLaunchKernelGGL((gemm_bf16_kernel<MODE, A_KC, B_KC, EPI, 256, 256>), dim3(grid), dim3(NT),
-                       0, st, g);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+hipError_t launch_tiles(int bm, int bn, int bk, int grid, const GemmArgs &g, hipStream_t st) {
+#define MOE_LAUNCH(BM_, BN_, BK_)                                                            \
+  if (bm == BM_ && bn == BN_ && bk == BK_) {                                              \
+    hipLaunchKernelGGL((gemm_bf16_kernel<MODE, A_KC, B_KC, EPI, BM_, BN_, BK_>), dim3(grid), \
+                       dim3(NT), 0, st, g);                                               \
+    return hipGetLastError();                                                             \
+  }
+  MOE_LAUNCH(128, 128, 64)
+  MOE_LAUNCH(128, 128, 32)
+#ifdef MOE_WIDE_TILES
+  MOE_LAUNCH(128, 256, 64)
+  MOE_LAUNCH(256, 128, 64)
+  MOE_LAUNCH(256, 256, 64)
+#endif
+#undef MOE_LAUNCH
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -479,20 +521,28 @@ hipError_t launch_tiles(int bm, int bn, int grid, const GemmArgs &g, hipStream_t
 #ifndef MOE_TILE_VK_BN
 #define MOE_TILE_VK_BN 128
 #endif
+#ifndef MOE_TILE_GM_BK
+#define MOE_TILE_GM_BK 64
+#endif
+#ifndef MOE_TILE_VK_BK
+#define MOE_TILE_VK_BK 32
+#endif
 
-void gemm_tile(GemmKind kind, const GemmArgs &g, int *bm, int *bn) {
+void gemm_tile(GemmKind kind, const GemmArgs &g, int *bm, int *bn, int *bk) {
   if (kind == kWeightGrad) {
     *bm = (g.M % MOE_TILE_VK_BM == 0) ? MOE_TILE_VK_BM : 128;
     *bn = (g.N % MOE_TILE_VK_BN == 0) ? MOE_TILE_VK_BN : 128;
+    *bk = MOE_TILE_VK_BK;
   } else {
     *bm = MOE_TILE_GM_BM;
     *bn = (g.N % MOE_TILE_GM_BN == 0) ? MOE_TILE_GM_BN : 128;
+    *bk = (g.K % MOE_TILE_GM_BK == 0) ? MOE_TILE_GM_BK : 32;
   }
 }
 
 int gemm_grid(GemmKind kind, const GemmArgs &g) {
-  int bm, bn;
-  gemm_tile(kind, g, &bm, &bn);
+  int bm, bn, bk;
+  gemm_tile(kind, g, &bm, &bn, &bk);
   if (kind == kWeightGrad) return g.E * (g.M / bm) * (g.N / bn);
   const int64_t mt = ((int64_t)g.cap + (int64_t)g.E * (bm - 1)) / bm;
   const int64_t grid = mt * (g.N / bn);
@@ -503,19 +553,19 @@ hipError_t launch_gemm_bf16(GemmKind kind, const GemmArgs &g, hipStream_t st) {
   const int grid = gemm_grid(kind, g);
   if (grid < 0) return hipErrorInvalidValue;
   if (grid == 0) return hipSuccess;
-  int bm, bn;
-  gemm_tile(kind, g, &bm, &bn);
+  int bm, bn, bk;
+  gemm_tile(kind, g, &bm, &bn, &bk);
   switch (kind) {
     case kUpSwiGLU:
-      return launch_tiles<GROUPED_M, true, false, EPI_SWIGLU>(bm, bn, grid, g, st);
+      return launch_tiles<GROUPED_M, true, false, EPI_SWIGLU>(bm, bn, bk, grid, g, st);
     case kDown:
-      return launch_tiles<GROUPED_M, true, false, EPI_STORE>(bm, bn, grid, g, st);
+      return launch_tiles<GROUPED_M, true, false, EPI_STORE>(bm, bn, bk, grid, g, st);
     case kDownBwd:
-      return launch_tiles<GROUPED_M, true, true, EPI_DSWIGLU>(bm, bn, grid, g, st);
+      return launch_tiles<GROUPED_M, true, true, EPI_DSWIGLU>(bm, bn, bk, grid, g, st);
     case kUpBwd:
-      return launch_tiles<GROUPED_M, true, true, EPI_STORE>(bm, bn, grid, g, st);
+      return launch_tiles<GROUPED_M, true, true, EPI_STORE>(bm, bn, bk, grid, g, st);
     case kWeightGrad:
-      return launch_tiles<VARLEN_K, false, false, EPI_STORE>(bm, bn, grid, g, st);
+      return launch_tiles<VARLEN_K, false, false, EPI_STORE>(bm, bn, bk, grid, g, st);
     default:
       return hipErrorInvalidValue;
   }

@@ -67,8 +67,8 @@ struct GemmArgs {
 };
 
 constexpr int kGemmBM = 128, kGemmBN = 128, kGemmBK = 64;  // smallest tile; fp32 mode tile
-// bf16 tile shape chosen for a GEMM (BM, BN in {128, 256}) and its grid size (-1: too large)
-void gemm_tile(GemmKind kind, const GemmArgs &g, int *bm, int *bn);
+// bf16 tile shape chosen for a GEMM (BM x BN x BK) and its grid size (-1: too large)
+void gemm_tile(GemmKind kind, const GemmArgs &g, int *bm, int *bn, int *bk);
 int gemm_grid(GemmKind kind, const GemmArgs &g);
 int gemm_grid_f32(GemmKind kind, const GemmArgs &g);
 hipError_t launch_gemm_bf16(GemmKind kind, const GemmArgs &g, hipStream_t stream);
