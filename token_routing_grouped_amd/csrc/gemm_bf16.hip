@@ -34,7 +34,6 @@
 namespace moe {
 namespace {
 
-constexpr int NT = 256;
 constexpr int PADK = 8;   // extra elements per row of a reduction-contiguous tile [rows][BK]
 constexpr int PADC = 32;  // extra columns of an M/N-contiguous tile [BK][cols]
 
@@ -69,25 +68,30 @@ __device__ __forceinline__ bf16x8 frag_mn(const uint16_t *tile, int kbase, int c
   return __builtin_bit_cast(bf16x8, v);
 }
 
-template <int MODE, bool A_KC, bool B_KC, int EPI, int BM, int BN, int BK>
-__global__ __launch_bounds__(NT, (BM * BN > 128 * 128) ? 1 : (BK == 32 ? 3 : 2))
+// WGM x WGN waves per workgroup; NT threads
+template <int MODE, bool A_KC, bool B_KC, int EPI, int BM, int BN, int BK, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN,
+                             (BM * BN > 128 * 128 && WGM * WGN == 4) ? 1 : (BK == 32 ? 3 : 2))
 void gemm_bf16_kernel(GemmArgs g) {
-  constexpr int TM = BM / 64, TN = BN / 64;  // 32x32 sub-tiles per wave
-  constexpr int WM = BM / 2, WN = BN / 2;    // wave tile
+  constexpr int NT = 64 * WGM * WGN;
+  constexpr int WM = BM / WGM, WN = BN / WGN;  // wave tile
+  constexpr int TM = WM / 32, TN = WN / 32;    // 32x32 sub-tiles per wave
+  static_assert(TM >= 1 && TN >= 1 && (EPI != EPI_SWIGLU || TN % 2 == 0), "wave tile");
   using AS = TileShape<A_KC, BM, BK>;
   using BS = TileShape<B_KC, BN, BK>;
   constexpr int CPK = BK / 8;  // 16-byte chunks per row of a reduction-contiguous tile
   constexpr int STAGE = AS::elems + BS::elems;
   constexpr int CLD = BN + 8;  // C staging row stride (elements)
-  static_assert(BM * CLD <= 2 * STAGE, "C staging fits in the stage buffers");
-  static_assert(2 * STAGE * 2 >= (2 * MOE_MAX_EXPERTS + 2) * 4, "tile tables fit");
+  // one buffer holds the two stages, then the bf16 C tile for the plain store
+  constexpr int SMEM = (2 * STAGE > BM * CLD) ? 2 * STAGE : BM * CLD;
+  static_assert(SMEM * 2 >= (2 * MOE_MAX_EXPERTS + 2) * 4, "tile tables fit");
   constexpr int A_LD = BM * BK / (8 * NT);  // 16-byte chunks per thread per stage
   constexpr int B_LD = BN * BK / (8 * NT);
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM];
   int *s_pref = (int *)smem;  // expert tile table, used before the first stage is written
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   const int P = g.foff[g.E];
   const uint16_t *A = (const uint16_t *)g.A;
   const uint16_t *B = (const uint16_t *)g.B;
@@ -305,43 +309,49 @@ void gemm_bf16_kernel(GemmArgs g) {
   // work to arrive.
   u32x4 ra0[A_LD], rb0[B_LD], ra1[A_LD], rb1[B_LD];
   int ia0[A_LD], ib0[B_LD], ia1[A_LD], ib1[B_LD];  // varlen-K: rows of each set's next tile
-  if constexpr (MODE == VARLEN_K) {
-    MOE_ROWS(ia0, ib0, 0);
-    MOE_ROWS(ia1, ib1, BK);
-  }
-  if (nk > 0) MOE_LOAD(ra0, rb0, ia0, ib0, 0);
-  if (nk > 1) MOE_LOAD(ra1, rb1, ia1, ib1, BK);
-  if (nk > 0) MOE_STORE(ra0, rb0, 0);
-  if (nk > 2) MOE_LOAD(ra0, rb0, ia0, ib0, 2 * BK);
-  __syncthreads();
-  int kt = 0;
-  // steady state, free of branches so the wait counters only hold back the set
-  // being stored (its loads are two tiles old), never the set loaded after it
-  for (; kt + 4 < nk; kt += 2) {
-    MOE_COMPUTE(0);  // tile kt
-    MOE_STORE(ra1, rb1, 1);
-    MOE_LOAD(ra1, rb1, ia1, ib1, (kt + 3) * BK);
-    __syncthreads();
-    MOE_COMPUTE(1);  // tile kt+1
-    MOE_STORE(ra0, rb0, 0);
-    MOE_LOAD(ra0, rb0, ia0, ib0, (kt + 4) * BK);
-    __syncthreads();
-  }
-  // the last (at most four) tiles
-  for (; kt < nk; kt += 2) {
-    MOE_COMPUTE(0);
-    if (kt + 1 < nk) {
-      MOE_STORE(ra1, rb1, 1);
-      if (kt + 3 < nk) MOE_LOAD(ra1, rb1, ia1, ib1, (kt + 3) * BK);
+  // Every load of the prologue and of the steady loop is unconditional (k offsets of
+  // grouped-M are clamped to the last tile, varlen-K rows past the segment read as
+  // zeros), so the memory wait counters stay exact across the loop.
+  if (nk > 0) {
+    auto kof = [&](int t) { return (MODE == GROUPED_M ? min(t, nk - 1) : t) * BK; };
+    if constexpr (MODE == VARLEN_K) {
+      MOE_ROWS(ia0, ib0, 0);
+      MOE_ROWS(ia1, ib1, BK);
     }
+    MOE_LOAD(ra0, rb0, ia0, ib0, 0);
+    MOE_LOAD(ra1, rb1, ia1, ib1, kof(1));
+    MOE_STORE(ra0, rb0, 0);
+    MOE_LOAD(ra0, rb0, ia0, ib0, kof(2));
     __syncthreads();
-    if (kt + 1 < nk) {
-      MOE_COMPUTE(1);
-      if (kt + 2 < nk) {
-        MOE_STORE(ra0, rb0, 0);
-        if (kt + 4 < nk) MOE_LOAD(ra0, rb0, ia0, ib0, (kt + 4) * BK);
+    int kt = 0;
+    // steady state, free of branches: the wait before a stage store only holds back
+    // the set being stored (loaded two tiles earlier), not the set loaded after it
+    for (; kt + 4 < nk; kt += 2) {
+      MOE_COMPUTE(0);  // tile kt
+      MOE_STORE(ra1, rb1, 1);
+      MOE_LOAD(ra1, rb1, ia1, ib1, (kt + 3) * BK);
+      __syncthreads();
+      MOE_COMPUTE(1);  // tile kt+1
+      MOE_STORE(ra0, rb0, 0);
+      MOE_LOAD(ra0, rb0, ia0, ib0, (kt + 4) * BK);
+      __syncthreads();
+    }
+    // the last (at most four) tiles
+    for (; kt < nk; kt += 2) {
+      MOE_COMPUTE(0);
+      if (kt + 1 < nk) {
+        MOE_STORE(ra1, rb1, 1);
+        if (kt + 3 < nk) MOE_LOAD(ra1, rb1, ia1, ib1, (kt + 3) * BK);
       }
       __syncthreads();
+      if (kt + 1 < nk) {
+        MOE_COMPUTE(1);
+        if (kt + 2 < nk) {
+          MOE_STORE(ra0, rb0, 0);
+          if (kt + 4 < nk) MOE_LOAD(ra0, rb0, ia0, ib0, (kt + 4) * BK);
+        }
+        __syncthreads();
+      }
     }
   }
 #undef MOE_LOAD
@@ -413,7 +423,7 @@ void gemm_bf16_kernel(GemmArgs g) {
     const uint16_t *__restrict__ Hs = (const uint16_t *)g.Hs;
     const float *__restrict__ scores = g.scores;
     const int32_t *__restrict__ s_scatter = g.s_scatter;
-    float *red = (float *)smem;  // [2][BM] row partials of the two column waves (the
+    float *red = (float *)smem;  // [WGN][BM] row partials of the column waves (the
                                  // loop's final barrier has released the stages)
 #pragma unroll
     for (int mi = 0; mi < TM; mi++) {
@@ -482,25 +492,30 @@ void gemm_bf16_kernel(GemmArgs g) {
       if ((lane & 1) == 0) red[wn * BM + row] = rsum;
     }
     __syncthreads();
-    for (int r = tid; r < rows; r += NT)
-      g.partial[(int64_t)(row0 + r) * g.n_ntiles + nt] = red[r] + red[BM + r];
+    for (int r = tid; r < rows; r += NT) {
+      float v = red[r];
+#pragma unroll
+      for (int w = 1; w < WGN; w++) v += red[w * BM + r];
+      g.partial[(int64_t)(row0 + r) * g.n_ntiles + nt] = v;
+    }
   }
 }
 
 template <int MODE, bool A_KC, bool B_KC, int EPI>
 hipError_t launch_tiles(int bm, int bn, int bk, int grid, const GemmArgs &g, hipStream_t st) {
-#define MOE_LAUNCH(BM_, BN_, BK_)                                                            \
+#define MOE_LAUNCH(BM_, BN_, BK_, WGM_, WGN_)                                                \
   if (bm == BM_ && bn == BN_ && bk == BK_) {                                              \
-    hipLaunchKernelGGL((gemm_bf16_kernel<MODE, A_KC, B_KC, EPI, BM_, BN_, BK_>), dim3(grid), \
-                       dim3(NT), 0, st, g);                                               \
+    hipLaunchKernelGGL((gemm_bf16_kernel<MODE, A_KC, B_KC, EPI, BM_, BN_, BK_, WGM_, WGN_>), \
+                       dim3(grid), dim3(64 * WGM_ * WGN_), 0, st, g);                    \
     return hipGetLastError();                                                             \
   }
-  MOE_LAUNCH(128, 128, 64)
-  MOE_LAUNCH(128, 128, 32)
+  MOE_LAUNCH(128, 128, 64, 2, 2)
+  MOE_LAUNCH(128, 128, 32, 2, 2)
+  MOE_LAUNCH(256, 256, 64, 2, 4)
+  MOE_LAUNCH(256, 256, 32, 2, 4)
 #ifdef MOE_WIDE_TILES
-  MOE_LAUNCH(128, 256, 64)
-  MOE_LAUNCH(256, 128, 64)
-  MOE_LAUNCH(256, 256, 64)
+  MOE_LAUNCH(128, 256, 64, 2, 4)
+  MOE_LAUNCH(256, 128, 64, 4, 2)
 #endif
 #undef MOE_LAUNCH
   return hipErrorInvalidValue;
@@ -508,18 +523,13 @@ hipError_t launch_tiles(int bm, int bn, int bk, int grid, const GemmArgs &g, hip
 
 }  // namespace
 
-// Tile shape per GEMM: the larger tiles where the fixed dimensions allow them.
-#ifndef MOE_TILE_GM_BM
-#define MOE_TILE_GM_BM 128
+// Tile shape per GEMM: 256x256x32 with eight waves where the fixed dimensions allow it
+// (half the bytes per flop of 128x128), else 128x128.
+#ifndef MOE_GM_BIG
+#define MOE_GM_BIG 1
 #endif
-#ifndef MOE_TILE_GM_BN
-#define MOE_TILE_GM_BN 128
-#endif
-#ifndef MOE_TILE_VK_BM
-#define MOE_TILE_VK_BM 128
-#endif
-#ifndef MOE_TILE_VK_BN
-#define MOE_TILE_VK_BN 128
+#ifndef MOE_VK_BIG
+#define MOE_VK_BIG 1
 #endif
 #ifndef MOE_TILE_GM_BK
 #define MOE_TILE_GM_BK 64
@@ -530,13 +540,15 @@ hipError_t launch_tiles(int bm, int bn, int bk, int grid, const GemmArgs &g, hip
 
 void gemm_tile(GemmKind kind, const GemmArgs &g, int *bm, int *bn, int *bk) {
   if (kind == kWeightGrad) {
-    *bm = (g.M % MOE_TILE_VK_BM == 0) ? MOE_TILE_VK_BM : 128;
-    *bn = (g.N % MOE_TILE_VK_BN == 0) ? MOE_TILE_VK_BN : 128;
-    *bk = MOE_TILE_VK_BK;
+    const bool big = MOE_VK_BIG && g.M % 256 == 0 && g.N % 256 == 0;
+    *bm = big ? 256 : 128;
+    *bn = big ? 256 : 128;
+    *bk = big ? 32 : MOE_TILE_VK_BK;
   } else {
-    *bm = MOE_TILE_GM_BM;
-    *bn = (g.N % MOE_TILE_GM_BN == 0) ? MOE_TILE_GM_BN : 128;
-    *bk = (g.K % MOE_TILE_GM_BK == 0) ? MOE_TILE_GM_BK : 32;
+    const bool big = MOE_GM_BIG && g.N % 256 == 0 && g.K % 32 == 0;
+    *bm = big ? 256 : 128;
+    *bn = big ? 256 : 128;
+    *bk = big ? 32 : (g.K % MOE_TILE_GM_BK == 0 ? MOE_TILE_GM_BK : 32);
   }
 }
 
