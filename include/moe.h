@@ -144,16 +144,17 @@ const char *moe_status_string(moe_status s);
  * The kernels the three calls enqueue, in launch order. */
 typedef enum {
   MOE_KERNEL_META_HIST = 0,    /* moe_build_metadata: per-chunk expert histograms */
-  MOE_KERNEL_META_SCATTER = 1, /* moe_build_metadata: scan + stable scatter */
-  MOE_KERNEL_UP_SWIGLU = 2,    /* forward: gathered up-projection + SwiGLU */
-  MOE_KERNEL_DOWN = 3,         /* forward: down projection */
-  MOE_KERNEL_COMBINE = 4,      /* forward: weighted combine to [N,H] */
-  MOE_KERNEL_DOWN_BWD = 5,     /* backward: dout_g W_down^T + dSwiGLU + dscore partials */
-  MOE_KERNEL_WGRAD_DOWN = 6,   /* backward: dW_down */
-  MOE_KERNEL_UP_BWD = 7,       /* backward: dh W_up^T */
-  MOE_KERNEL_WGRAD_UP = 8,     /* backward: dW_up */
-  MOE_KERNEL_COMBINE_DX = 9,   /* backward: dx = sum over the token's rows */
-  MOE_KERNEL_DSCORE = 10,      /* backward: d_topk_weights in [N,K] */
+  MOE_KERNEL_META_SCAN = 1,    /* moe_build_metadata: prefixes over chunks, totals */
+  MOE_KERNEL_META_SCATTER = 2, /* moe_build_metadata: offsets + stable scatter */
+  MOE_KERNEL_UP_SWIGLU = 3,    /* forward: gathered up-projection + SwiGLU */
+  MOE_KERNEL_DOWN = 4,         /* forward: down projection */
+  MOE_KERNEL_COMBINE = 5,      /* forward: weighted combine to [N,H] */
+  MOE_KERNEL_DOWN_BWD = 6,     /* backward: dout_g W_down^T + dSwiGLU + dscore partials */
+  MOE_KERNEL_WGRAD_DOWN = 7,   /* backward: dW_down */
+  MOE_KERNEL_UP_BWD = 8,       /* backward: dh W_up^T */
+  MOE_KERNEL_WGRAD_UP = 9,     /* backward: dW_up */
+  MOE_KERNEL_COMBINE_DX = 10,  /* backward: dx = sum over the token's rows, and
+                                  d_topk_weights in [N,K] */
   MOE_KERNEL_COUNT = 11
 } moe_kernel_id;
 

@@ -23,8 +23,8 @@ EXPORTED_SYMBOLS = [
     "moe_expert_backward_workspace", "moe_build_metadata", "moe_expert_forward",
     "moe_expert_backward", "moe_status_string", "moe_time_kernel", "moe_kernel_name",
 ]
-KERNELS = ["meta_hist", "meta_scatter", "up_swiglu", "down", "combine", "down_bwd",
-           "wgrad_down", "up_bwd", "wgrad_up", "combine_dx", "dscore"]
+KERNELS = ["meta_hist", "meta_scan", "meta_scatter", "up_swiglu", "down", "combine", "down_bwd",
+           "wgrad_down", "up_bwd", "wgrad_up", "combine_dx"]
 
 
 class MoeError(RuntimeError):

@@ -145,6 +145,11 @@ moe_status moe_build_metadata(const int32_t *topk_idx, const float *topk_weights
     err = launch_meta_hist(topk_idx, meta->N, meta->K, meta->E, (int32_t *)workspace, st);
   }
   if (err != hipSuccess) return MOE_EHIP;
+  {
+    Bracket b(MOE_KERNEL_META_SCAN, st);
+    err = launch_meta_scan(meta->N, meta->K, meta->E, (int32_t *)workspace, st);
+  }
+  if (err != hipSuccess) return MOE_EHIP;
   Bracket b(MOE_KERNEL_META_SCATTER, st);
   err = launch_meta_scatter(topk_idx, topk_weights, meta->N, meta->K, meta->E, meta->capacity,
                             (const int32_t *)workspace, o, st);
@@ -292,18 +297,12 @@ moe_status moe_expert_backward(const moe_metadata *meta, const int32_t *topk_idx
   g.c_es = (int64_t)H * 2 * I;
   if ((s = gemm(kWeightGrad, MOE_KERNEL_WGRAD_UP, g, dt, st)) != MOE_OK) return s;
   if (meta->N == 0) return MOE_OK;
-  // dx = sum_q dxg[s_rev[q]]; d_topk_weights from the partials
-  hipError_t err;
-  {
-    Bracket b(MOE_KERNEL_COMBINE_DX, st);
-    err = launch_combine(dt == MOE_BF16, dxg, meta->num_activated_expert_per_token_offset,
-                         meta->s_reverse_scatter_idx, nullptr, meta->N, H, meta->capacity, dx, st);
-  }
-  if (err != hipSuccess) return MOE_EHIP;
-  Bracket b(MOE_KERNEL_DSCORE, st);
-  err = launch_dscore(topk_idx, meta->N, meta->K, meta->E,
-                      meta->num_activated_expert_per_token_offset, meta->s_reverse_scatter_idx,
-                      partial, nnt, meta->capacity, d_topk_weights, st);
+  // dx = sum_q dxg[s_rev[q]], and d_topk_weights from the partials
+  Bracket b(MOE_KERNEL_COMBINE_DX, st);
+  hipError_t err = launch_combine_dscore(
+      dt == MOE_BF16, dxg, meta->num_activated_expert_per_token_offset,
+      meta->s_reverse_scatter_idx, meta->N, H, meta->capacity, dx, topk_idx, meta->K, meta->E,
+      partial, nnt, d_topk_weights, st);
   return err == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
@@ -323,8 +322,8 @@ moe_status moe_time_kernel(moe_kernel_id kernel, void *const *events, int32_t n_
 
 const char *moe_kernel_name(moe_kernel_id k) {
   static const char *names[MOE_KERNEL_COUNT] = {
-      "meta_hist", "meta_scatter", "up_swiglu", "down", "combine", "down_bwd",
-      "wgrad_down", "up_bwd", "wgrad_up", "combine_dx", "dscore"};
+      "meta_hist", "meta_scan", "meta_scatter", "up_swiglu", "down", "combine", "down_bwd",
+      "wgrad_down", "up_bwd", "wgrad_up", "combine_dx"};
   return ((int)k >= 0 && (int)k < MOE_KERNEL_COUNT) ? names[(int)k] : "unknown";
 }
 

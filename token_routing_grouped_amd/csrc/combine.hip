@@ -7,116 +7,130 @@
 // walks the token's pairs in ascending pair order (the CSR row pointer
 // num_activated_expert_per_token_offset) and sums in fp32 with one final
 // rounding: deterministic, no atomics, every output row written once.
+//
+// The wavefront first loads the token's pair metadata lane-parallel (lane j holds
+// pair q0+j: its sorted position and weight), then streams the expert rows with
+// several pairs' loads in flight. The backward variant also writes the token's
+// row of d_topk_weights (issue #68, question 4: router gradients in [N,K]): slot k
+// of a valid expert id is the token's (number of valid slots before k)-th pair,
+// and its gradient is the sum, in tile order, of the per-column-tile partials the
+// down-projection backward wrote for that pair.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 namespace {
 
-constexpr int CT = 256;  // 4 tokens per workgroup, one wave each
-constexpr int CHUNKS = 4;  // 16-byte chunks per lane kept in flight
+constexpr int CT = 256;    // 4 tokens per workgroup, one wave each
+constexpr int CHUNKS = 4;  // 16-byte chunks per lane per pass over the row
+constexpr int PAIRS = 2;   // pairs whose rows are loaded together
 
 template <typename T>
 struct Vec;
 template <>
 struct Vec<uint16_t> {  // bf16: 8 elements per 16 bytes
   static constexpr int n = 8;
-  __device__ static void to_f32(const uint4 &v, float *f) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  __device__ static void add(const u32x4 &v, float w, float *f) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      f[2 * i] = bf16_to_f32((uint16_t)(w[i] & 0xffffu));
-      f[2 * i + 1] = bf16_to_f32((uint16_t)(w[i] >> 16));
+      f[2 * i] += w * bf16_to_f32((uint16_t)(v[i] & 0xffffu));
+      f[2 * i + 1] += w * bf16_to_f32((uint16_t)(v[i] >> 16));
     }
   }
-  __device__ static uint4 from_f32(const float *f) {
-    return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
-                      pack_bf16x2(f[6], f[7]));
+  __device__ static u32x4 pack(const float *f) {
+    return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                 pack_bf16x2(f[6], f[7])};
   }
 };
 template <>
 struct Vec<float> {  // fp32: 4 elements per 16 bytes
   static constexpr int n = 4;
-  __device__ static void to_f32(const uint4 &v, float *f) {
-    f[0] = __uint_as_float(v.x);
-    f[1] = __uint_as_float(v.y);
-    f[2] = __uint_as_float(v.z);
-    f[3] = __uint_as_float(v.w);
+  __device__ static void add(const u32x4 &v, float w, float *f) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) f[i] += w * __uint_as_float(v[i]);
   }
-  __device__ static uint4 from_f32(const float *f) {
-    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
-                      __float_as_uint(f[3]));
+  __device__ static u32x4 pack(const float *f) {
+    return u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                 __float_as_uint(f[3])};
   }
 };
 
-template <typename T>
+struct DscoreArgs {
+  const int32_t *topk_idx;
+  int K, E;
+  const float *partial;
+  int nnt;
+  float *dtw;
+};
+
+template <typename T, bool DSCORE>
 __global__ __launch_bounds__(CT) void combine_kernel(const T *__restrict__ y,
                                                     const int32_t *__restrict__ tok_off,
                                                     const int32_t *__restrict__ s_rev,
                                                     const float *__restrict__ scores, int N,
-                                                    int H, int cap, T *__restrict__ out) {
+                                                    int H, int cap, T *__restrict__ out,
+                                                    DscoreArgs ds) {
   constexpr int V = Vec<T>::n;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (CT / 64) + (threadIdx.x >> 6);
   if (t >= N) return;
   const bool over = tok_off[N] > cap;
   const int q0 = tok_off[t];
-  const int q1 = over ? q0 : tok_off[t + 1];
+  const int n = over ? 0 : tok_off[t + 1] - q0;  // pairs of this token (<= K <= 64)
+  // lane j: the j-th pair's sorted position and weight
+  const int my_s = lane < n ? s_rev[q0 + lane] : 0;
+  const float my_w = lane < n ? (scores ? scores[q0 + lane] : 1.0f) : 0.0f;
+
   const int nchunk = H / V;
-  uint4 *orow = (uint4 *)(out + (int64_t)t * H);
+  u32x4 *orow = (u32x4 *)(out + (int64_t)t * H);
   for (int c0 = 0; c0 < nchunk; c0 += 64 * CHUNKS) {
     float acc[CHUNKS][V];
 #pragma unroll
     for (int i = 0; i < CHUNKS; i++)
 #pragma unroll
       for (int v = 0; v < V; v++) acc[i][v] = 0.0f;
-    for (int q = q0; q < q1; q++) {
-      const int s = s_rev[q];
-      const float w = scores ? scores[q] : 1.0f;
-      const uint4 *yrow = (const uint4 *)(y + (int64_t)s * H);
-      uint4 raw[CHUNKS];
+    for (int j0 = 0; j0 < n; j0 += PAIRS) {
+      u32x4 raw[PAIRS][CHUNKS];
+      float w[PAIRS];
 #pragma unroll
-      for (int i = 0; i < CHUNKS; i++) {
-        const int c = c0 + i * 64 + lane;
-        raw[i] = c < nchunk ? yrow[c] : make_uint4(0, 0, 0, 0);
+      for (int p = 0; p < PAIRS; p++) {
+        const int j = j0 + p < n ? j0 + p : j0;  // a missing second pair re-reads the first
+        const int s = __shfl(my_s, j, kWave);
+        w[p] = __shfl(my_w, j, kWave);
+        const u32x4 *yrow = (const u32x4 *)(y + (int64_t)s * H);
+#pragma unroll
+        for (int i = 0; i < CHUNKS; i++) {
+          const int c = c0 + i * 64 + lane;
+          raw[p][i] = c < nchunk ? yrow[c] : u32x4{0, 0, 0, 0};
+        }
       }
+      // ascending pair order within and across groups
 #pragma unroll
-      for (int i = 0; i < CHUNKS; i++) {
-        float f[V];
-        Vec<T>::to_f32(raw[i], f);
+      for (int p = 0; p < PAIRS; p++) {
+        if (j0 + p >= n) break;  // wave-uniform
 #pragma unroll
-        for (int v = 0; v < V; v++) acc[i][v] += w * f[v];
+        for (int i = 0; i < CHUNKS; i++) Vec<T>::add(raw[p][i], w[p], acc[i]);
       }
     }
 #pragma unroll
     for (int i = 0; i < CHUNKS; i++) {
       const int c = c0 + i * 64 + lane;
-      if (c < nchunk) orow[c] = Vec<T>::from_f32(acc[i]);
+      if (c < nchunk) orow[c] = Vec<T>::pack(acc[i]);
     }
   }
-}
 
-__global__ __launch_bounds__(256) void dscore_kernel(const int32_t *__restrict__ idx, int N,
-                                                     int K, int E,
-                                                     const int32_t *__restrict__ tok_off,
-                                                     const int32_t *__restrict__ s_rev,
-                                                     const float *__restrict__ partial, int nnt,
-                                                     int cap, float *__restrict__ dtw) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= N) return;
-  const bool over = tok_off[N] > cap;
-  int q = tok_off[t];
-  for (int k = 0; k < K; k++) {
-    const int e = idx[(int64_t)t * K + k];
+  if constexpr (DSCORE) {
+    const int K = ds.K;
+    const int e = lane < K ? ds.topk_idx[(int64_t)t * K + lane] : -1;
+    const bool valid = (unsigned)e < (unsigned)ds.E;
+    const uint64_t vm = ballot64(valid);
     float v = 0.0f;
-    if ((unsigned)e < (unsigned)E) {
-      if (!over) {
-        const float *p = partial + (int64_t)s_rev[q] * nnt;
-        for (int i = 0; i < nnt; i++) v += p[i];
-      }
-      q++;
+    if (valid && !over) {
+      const int s = s_rev[q0 + popc_below(vm)];
+      const float *p = ds.partial + (int64_t)s * ds.nnt;
+      for (int i = 0; i < ds.nnt; i++) v += p[i];
     }
-    dtw[(int64_t)t * K + k] = v;
+    if (lane < K) ds.dtw[(int64_t)t * K + lane] = v;
   }
 }
 
@@ -127,21 +141,31 @@ hipError_t launch_combine(bool bf16, const void *y, const int32_t *tok_off, cons
                           hipStream_t stream) {
   if (N == 0) return hipSuccess;
   const int grid = (N + 3) / 4;
+  DscoreArgs ds = {};
   if (bf16)
-    hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(grid), dim3(CT), 0, stream,
-                       (const uint16_t *)y, tok_off, s_rev, scores, N, H, cap, (uint16_t *)out);
+    hipLaunchKernelGGL((combine_kernel<uint16_t, false>), dim3(grid), dim3(CT), 0, stream,
+                       (const uint16_t *)y, tok_off, s_rev, scores, N, H, cap, (uint16_t *)out,
+                       ds);
   else
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(grid), dim3(CT), 0, stream, (const float *)y,
-                       tok_off, s_rev, scores, N, H, cap, (float *)out);
+    hipLaunchKernelGGL((combine_kernel<float, false>), dim3(grid), dim3(CT), 0, stream,
+                       (const float *)y, tok_off, s_rev, scores, N, H, cap, (float *)out, ds);
   return hipGetLastError();
 }
 
-hipError_t launch_dscore(const int32_t *topk_idx, int N, int K, int E, const int32_t *tok_off,
-                         const int32_t *s_rev, const float *partial, int n_ntiles, int cap,
-                         float *d_topk_weights, hipStream_t stream) {
+hipError_t launch_combine_dscore(bool bf16, const void *dxg, const int32_t *tok_off,
+                                 const int32_t *s_rev, int N, int H, int cap, void *dx,
+                                 const int32_t *topk_idx, int K, int E, const float *partial,
+                                 int n_ntiles, float *d_topk_weights, hipStream_t stream) {
   if (N == 0) return hipSuccess;
-  hipLaunchKernelGGL(dscore_kernel, dim3((N + 255) / 256), dim3(256), 0, stream, topk_idx, N, K,
-                     E, tok_off, s_rev, partial, n_ntiles, cap, d_topk_weights);
+  const int grid = (N + 3) / 4;
+  DscoreArgs ds = {topk_idx, K, E, partial, n_ntiles, d_topk_weights};
+  if (bf16)
+    hipLaunchKernelGGL((combine_kernel<uint16_t, true>), dim3(grid), dim3(CT), 0, stream,
+                       (const uint16_t *)dxg, tok_off, s_rev, nullptr, N, H, cap,
+                       (uint16_t *)dx, ds);
+  else
+    hipLaunchKernelGGL((combine_kernel<float, true>), dim3(grid), dim3(CT), 0, stream,
+                       (const float *)dxg, tok_off, s_rev, nullptr, N, H, cap, (float *)dx, ds);
   return hipGetLastError();
 }
 

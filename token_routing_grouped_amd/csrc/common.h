@@ -39,14 +39,17 @@ __device__ __forceinline__ int popc_below(uint64_t m) {
 }
 __device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
 
-// Inclusive prefix sum across the 64 lanes of a wave.
-__device__ __forceinline__ int wave_inclusive_scan(int v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int t = __shfl_up(v, o, kWave);
-    if (lane >= o) v += t;
-  }
+// Inclusive prefix sum across the 64 lanes of a wave with DPP lane moves (no LDS
+// traffic): Hillis-Steele shifts 1, 2, 4, 8 inside each row of 16 lanes, then
+// lane 15 of rows 0 and 2 is added into rows 1 and 3, then lane 31 into rows 2
+// and 3 (GFX9 DPP row_shr, row_bcast:15, row_bcast:31). All 64 lanes must be active.
+__device__ __forceinline__ int wave_inclusive_scan_dpp(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false); // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false); // row_bcast:31 -> rows 2, 3
   return v;
 }
 
@@ -60,7 +63,7 @@ __device__ __forceinline__ void wave0_exclusive_scan(int *a, int n) {
   const int hi = lo + per < n ? lo + per : n;
   int s = 0;
   for (int i = lo; i < hi; i++) s += a[i];
-  const int incl = wave_inclusive_scan(s);
+  const int incl = wave_inclusive_scan_dpp(s);
   int run = incl - s;
   for (int i = lo; i < hi; i++) {
     const int v = a[i];

@@ -71,7 +71,7 @@ __device__ __forceinline__ bf16x8 frag_mn(const uint16_t *tile, int kbase, int c
 // WGM x WGN waves per workgroup; NT threads
 template <int MODE, bool A_KC, bool B_KC, int EPI, int BM, int BN, int BK, int WGM, int WGN>
 __global__ __launch_bounds__(64 * WGM * WGN,
-                             (BM * BN > 128 * 128 && WGM * WGN == 4) ? 1 : (BK == 32 ? 3 : 2))
+                             (BM * BN > 128 * 128) ? (WGM * WGN == 8 ? 2 : 1) : (BK == 32 ? 3 : 2))
 void gemm_bf16_kernel(GemmArgs g) {
   constexpr int NT = 64 * WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;  // wave tile

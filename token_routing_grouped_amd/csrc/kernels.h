@@ -7,7 +7,10 @@ namespace moe {
 
 // ---- routing metadata -------------------------------------------------------
 constexpr int kMetaThreads = 256;
-constexpr int kMetaItems = 8;                           // slots per thread
+#ifndef MOE_META_ITEMS
+#define MOE_META_ITEMS 2
+#endif
+constexpr int kMetaItems = MOE_META_ITEMS;              // slots per thread
 constexpr int kMetaChunk = kMetaThreads * kMetaItems;  // slots per workgroup
 
 struct MetaOut {
@@ -21,13 +24,30 @@ inline int meta_blocks(int64_t NK) {
   int64_t b = (NK + kMetaChunk - 1) / kMetaChunk;
   return b < 1 ? 1 : (int)b;
 }
-inline size_t meta_workspace_bytes(int64_t NK, int E) {
-  return (size_t)meta_blocks(NK) * (size_t)(E + 1) * sizeof(int32_t);
+// metadata workspace, in int32 elements: per-chunk histogram columns [E+2][nblk],
+// per-chunk exclusive prefixes [nblk][E+2], column totals [E+2]
+struct MetaWs {
+  int nblk;
+  size_t hist, pre, tot, total;
+};
+inline MetaWs meta_ws_layout(int64_t NK, int E) {
+  MetaWs L;
+  L.nblk = meta_blocks(NK);
+  const size_t cells = (size_t)L.nblk * (size_t)(E + 2);
+  L.hist = 0;
+  L.pre = cells;
+  L.tot = 2 * cells;
+  L.total = 2 * cells + (size_t)(E + 2);
+  return L;
 }
-hipError_t launch_meta_hist(const int32_t *topk_idx, int N, int K, int E, int32_t *hist_ws,
+inline size_t meta_workspace_bytes(int64_t NK, int E) {
+  return meta_ws_layout(NK, E).total * sizeof(int32_t);
+}
+hipError_t launch_meta_hist(const int32_t *topk_idx, int N, int K, int E, int32_t *ws,
                             hipStream_t stream);
+hipError_t launch_meta_scan(int N, int K, int E, int32_t *ws, hipStream_t stream);
 hipError_t launch_meta_scatter(const int32_t *topk_idx, const float *topk_weights, int N, int K,
-                               int E, int capacity, const int32_t *hist_ws, const MetaOut &out,
+                               int E, int capacity, const int32_t *ws, const MetaOut &out,
                                hipStream_t stream);
 
 // ---- grouped GEMMs (bf16 MFMA) ----------------------------------------------
@@ -80,9 +100,11 @@ hipError_t launch_gemm_f32(GemmKind kind, const GemmArgs &g, hipStream_t stream)
 hipError_t launch_combine(bool bf16, const void *y, const int32_t *tok_off,
                           const int32_t *s_rev, const float *scores, int N, int H, int cap,
                           void *out, hipStream_t stream);
-// d_topk_weights[t,k] = sum over tiles of partial[s_rev[q],tile] at valid slots, else 0.
-hipError_t launch_dscore(const int32_t *topk_idx, int N, int K, int E, const int32_t *tok_off,
-                         const int32_t *s_rev, const float *partial, int n_ntiles, int cap,
-                         float *d_topk_weights, hipStream_t stream);
+// The same for dx with unit weights, also writing d_topk_weights[t,k] = the sum over
+// column tiles of partial[s_rev[q],tile] for the slot's pair q (0 at invalid slots).
+hipError_t launch_combine_dscore(bool bf16, const void *dxg, const int32_t *tok_off,
+                                 const int32_t *s_rev, int N, int H, int cap, void *dx,
+                                 const int32_t *topk_idx, int K, int E, const float *partial,
+                                 int n_ntiles, float *d_topk_weights, hipStream_t stream);
 
 }  // namespace moe

@@ -7,15 +7,19 @@
 // token-major with ascending slot; the sort is a stable counting sort, so the
 // result is unique.
 //
-// Two kernels:
-//  1. meta_hist: each workgroup counts its chunk of slots per expert (LDS
-//     integer atomics) and flags ids outside [-1,E).
-//  2. meta_scatter: each workgroup sums the histograms of all chunks (column
-//     totals give expert_frequency and its scan; the chunks before it give its
-//     base per expert), then ranks its own slots stably: inside a wavefront the
-//     lanes holding the same expert are found with one ballot per expert-id bit
-//     and ranked with mbcnt; per-wave running counts in LDS order the rounds and
-//     the four waves. Every output index is written exactly once.
+// The slots are cut into chunks of kMetaChunk; three kernels:
+//  1. meta_hist: each workgroup counts its chunk per expert (LDS integer atomics),
+//     flags ids outside [-1,E) and counts its valid slots. Columns: E experts,
+//     the flag, the valid count; stored column-major [E+2][nblk].
+//  2. meta_scan: one workgroup per column: exclusive prefix over chunks (each
+//     thread sums a run of consecutive chunks, then DPP scans inside wavefronts),
+//     stored row-major [nblk][E+2], and the column total.
+//  3. meta_scatter: each workgroup reads its row of prefixes and the totals (one
+//     memory round trip), scans the totals into expert_frequency_offset, then
+//     ranks its own slots stably: inside a wavefront the lanes holding the same
+//     expert are found with one ballot per expert-id bit and ranked with mbcnt;
+//     per-wave running counts in LDS order the rounds and the four waves. Every
+//     output index is written exactly once.
 #include "common.h"
 #include "kernels.h"
 #include "../../include/moe.h"
@@ -25,8 +29,8 @@ namespace moe {
 __global__ __launch_bounds__(kMetaThreads) void meta_hist_kernel(const int32_t *__restrict__ idx,
                                                                  int64_t NK, int E,
                                                                  int32_t *__restrict__ hist) {
-  extern __shared__ int32_t sh[];  // [E+1]: counts, then the bad-id flag
-  for (int e = threadIdx.x; e <= E; e += kMetaThreads) sh[e] = 0;
+  extern __shared__ int32_t sh[];  // [E+2]: counts, bad-id flag, valid count
+  for (int e = threadIdx.x; e < E + 2; e += kMetaThreads) sh[e] = 0;
   __syncthreads();
   const int64_t base = (int64_t)blockIdx.x * kMetaChunk + threadIdx.x;
   int v[kMetaItems];
@@ -35,92 +39,142 @@ __global__ __launch_bounds__(kMetaThreads) void meta_hist_kernel(const int32_t *
     const int64_t j = base + (int64_t)i * kMetaThreads;
     v[i] = j < NK ? idx[j] : -1;
   }
-  int bad = 0;
+  int bad = 0, nvalid = 0;
 #pragma unroll
   for (int i = 0; i < kMetaItems; i++) {
-    if ((unsigned)v[i] < (unsigned)E)
+    const bool ok = (unsigned)v[i] < (unsigned)E;
+    if (ok)
       atomicAdd(&sh[v[i]], 1);
     else if (v[i] != -1)
       bad = 1;
+    nvalid += __builtin_popcountll(ballot64(ok));
   }
   if (bad) atomicOr(&sh[E], 1);
+  if (lane_id() == 0) atomicAdd(&sh[E + 1], nvalid);
   __syncthreads();
-  int32_t *row = hist + (int64_t)blockIdx.x * (E + 1);
-  for (int e = threadIdx.x; e <= E; e += kMetaThreads) row[e] = sh[e];
+  for (int e = threadIdx.x; e < E + 2; e += kMetaThreads)
+    hist[(int64_t)e * gridDim.x + blockIdx.x] = sh[e];
+}
+
+// One workgroup per column c of hist: pre[b][c] = sum of hist[c][b'] over b' < b,
+// tot[c] = the column's sum. Thread i covers chunks [i*R, i*R+R); the thread sums
+// are scanned with DPP inside each wavefront and the four wavefront totals in LDS.
+__global__ __launch_bounds__(kMetaThreads) void meta_scan_kernel(const int32_t *__restrict__ hist,
+                                                                 int W, int nblk,
+                                                                 int32_t *__restrict__ pre,
+                                                                 int32_t *__restrict__ tot) {
+  __shared__ int32_t s_wave[kMetaThreads / kWave];
+  const int c = blockIdx.x;
+  const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
+  const int R = (nblk + kMetaThreads - 1) / kMetaThreads;
+  const int b0 = tid * R;
+  const int32_t *col = hist + (int64_t)c * nblk;
+  constexpr int kReg = 8;
+  int v[kReg];
+  int s = 0;
+  if (R <= kReg) {
+#pragma unroll
+    for (int r = 0; r < kReg; r++) v[r] = (r < R && b0 + r < nblk) ? col[b0 + r] : 0;
+#pragma unroll
+    for (int r = 0; r < kReg; r++) s += v[r];
+  } else {
+    for (int r = 0; r < R && b0 + r < nblk; r++) s += col[b0 + r];
+  }
+  const int incl = wave_inclusive_scan_dpp(s);
+  if (lane == kWave - 1) s_wave[w] = incl;
+  __syncthreads();
+  int run = incl - s, total = 0;
+#pragma unroll
+  for (int i = 0; i < kMetaThreads / kWave; i++) {
+    const int t = s_wave[i];
+    run += i < w ? t : 0;
+    total += t;
+  }
+  if (R <= kReg) {
+#pragma unroll
+    for (int r = 0; r < kReg; r++) {
+      if (r < R && b0 + r < nblk) pre[(int64_t)(b0 + r) * W + c] = run;
+      run += v[r];
+    }
+  } else {  // long runs: a second pass over the (cached) run
+    for (int r = 0; r < R && b0 + r < nblk; r++) {
+      pre[(int64_t)(b0 + r) * W + c] = run;
+      run += col[b0 + r];
+    }
+  }
+  if (tid == 0) tot[c] = total;
 }
 
 __global__ __launch_bounds__(kMetaThreads) void meta_scatter_kernel(
     const int32_t *__restrict__ idx, const float *__restrict__ wts, int N, int K, int E,
-    int nbits, int nblk, int cap, const int32_t *__restrict__ hist, MetaOut out) {
+    int nbits, int cap, const int32_t *__restrict__ pre, const int32_t *__restrict__ tot,
+    MetaOut out) {
   extern __shared__ int32_t sh[];
-  int32_t *s_total = sh;                // [E+2]: column totals, then flag; scanned in place
-  int32_t *s_before = s_total + E + 2;  // [E+1]: counts in earlier chunks -> bases
-  int32_t *s_run = s_before + E + 1;    // [4][E] per-wave running counts
-  int32_t *s_misc = s_run + 4 * E;      // [8]: per-wave valid counts, valid-before, flag
+  int32_t *s_off = sh;              // [E+2]: totals, scanned in place -> offsets, [E] = P,
+                                    // [E+1] = bad-id flags
+  int32_t *s_base = s_off + E + 2;  // [E+2]: this chunk's prefix row -> bases
+  int32_t *s_run = s_base + E + 2;  // [4][E] per-wave running counts
+  int32_t *s_misc = s_run + 4 * E;  // [8]: per-wave valid counts
   const int tid = threadIdx.x;
+  const int w = tid / kWave;
+  const int lane = tid % kWave;
   const int64_t NK = (int64_t)N * K;
-
-  for (int i = tid; i < 2 * E + 3 + 4 * E + 8; i += kMetaThreads) sh[i] = 0;
-  __syncthreads();
-
-  // column sums over all chunks' histograms
-  const int W = E + 1;
-  const int tot = nblk * W;  // < 2^31, checked by the host
   const int me = blockIdx.x;
-  for (int i = tid; i < tot; i += kMetaThreads) {
-    const int b = i / W;
-    const int e = i - b * W;
-    const int v = hist[i];
-    if (v == 0) continue;
-    if (e < E) {
-      atomicAdd(&s_total[e], v);
-      if (b < me) atomicAdd(&s_before[e], v);
-    } else {
-      atomicOr(&s_misc[5], v);
+  const int W = E + 2;
+
+  // this wave's slots (the w-th quarter of the chunk, rounds of 64), the chunk's
+  // prefix row and the totals: all loads issued together
+  const int64_t wbase = (int64_t)me * kMetaChunk + (int64_t)w * (kMetaChunk / 4);
+  int r_e[kMetaItems];
+  float r_w[kMetaItems];
+#pragma unroll
+  for (int it = 0; it < kMetaItems; it++) {
+    const int64_t j = wbase + it * kWave + lane;
+    r_e[it] = j < NK ? idx[j] : -1;
+    r_w[it] = j < NK ? wts[j] : 0.0f;
+  }
+  const int32_t *prow = pre + (int64_t)me * W;
+  for (int c = tid; c < W; c += kMetaThreads) {
+    s_base[c] = prow[c];
+    if (c <= E) {
+      const int t = tot[c];
+      s_off[c < E ? c : E + 1] = t;
+      if (me == 0 && c < E) out.expert_frequency[c] = t;
     }
   }
+  for (int i = tid; i < 4 * E + 8; i += kMetaThreads) s_run[i] = 0;
   __syncthreads();
-  for (int e = tid; e < E; e += kMetaThreads)
-    if (s_before[e]) atomicAdd(&s_misc[4], s_before[e]);  // valid pairs before this chunk
-  if (me == 0)
-    for (int e = tid; e < E; e += kMetaThreads) out.expert_frequency[e] = s_total[e];
+  wave0_exclusive_scan(s_off, E);  // s_off[e] = expert_frequency_offset[e], [E] = P
   __syncthreads();
-  wave0_exclusive_scan(s_total, E);  // s_total[e] = expert_frequency_offset[e], [E] = P
-  __syncthreads();
-  const int P = s_total[E];
+  const int P = s_off[E];
   if (me == 0) {
-    for (int e = tid; e <= E; e += kMetaThreads) out.expert_frequency_offset[e] = s_total[e];
+    for (int e = tid; e <= E; e += kMetaThreads) out.expert_frequency_offset[e] = s_off[e];
     if (tid == 0) {
       out.tok_off[N] = P;
       uint32_t st = 0;
-      if (s_misc[5]) st |= MOE_DEV_BAD_EXPERT;
+      if (s_off[E + 1]) st |= MOE_DEV_BAD_EXPERT;
       if (P > cap) st |= MOE_DEV_OVER_CAPACITY;
       *out.status = st;
     }
   }
-  for (int e = tid; e < E; e += kMetaThreads) s_before[e] += s_total[e];  // base of this chunk
-  const int valid_before = s_misc[4];
+  const int valid_before = s_base[E + 1];
+  for (int e = tid; e < E; e += kMetaThreads) s_base[e] += s_off[e];  // base of this chunk
 
-  // ---- stable in-chunk ranks: wave w owns the w-th quarter of the chunk, in rounds of 64
-  const int w = tid / kWave;
-  const int lane = tid % kWave;
-  const int64_t wbase = (int64_t)me * kMetaChunk + (int64_t)w * (kMetaChunk / 4);
-  int r_e[kMetaItems], r_rank[kMetaItems], r_vrank[kMetaItems];
-  float r_w[kMetaItems];
+  // ---- stable in-chunk ranks
+  int r_rank[kMetaItems], r_vrank[kMetaItems];
   int vrun = 0;
   int32_t *run = s_run + w * E;
 #pragma unroll
   for (int it = 0; it < kMetaItems; it++) {
-    const int64_t j = wbase + it * kWave + lane;
-    int e = j < NK ? idx[j] : -1;
-    r_w[it] = j < NK ? wts[j] : 0.0f;
+    const int e = r_e[it];
     const bool v = (unsigned)e < (unsigned)E;
     const uint64_t vm = ballot64(v);
+    // lanes of this round holding the same expert: agree with e on every id bit
     uint64_t m = vm;
     for (int b = 0; b < nbits; b++) {
-      const bool bit = v && ((e >> b) & 1);
-      const uint64_t bm = ballot64(bit);
-      m &= bit ? bm : ~bm;
+      const uint64_t bm = ballot64(v && ((e >> b) & 1));
+      const uint64_t S = (uint64_t)(int64_t)(-((e >> b) & 1));  // all ones where the bit is set
+      m &= S ^ ~bm;                                               // bit set: bm, else ~bm
     }
     int prev = 0;
     if (v) prev = run[e];
@@ -136,45 +190,54 @@ __global__ __launch_bounds__(kMetaThreads) void meta_scatter_kernel(
 
   int vbase = valid_before;
   for (int w2 = 0; w2 < w; w2++) vbase += s_misc[w2];
+  const bool small = NK <= 0x7fffffff;
 #pragma unroll
   for (int it = 0; it < kMetaItems; it++) {
     const int64_t j = wbase + it * kWave + lane;
     if (j >= NK) break;
     const int q = vbase + r_vrank[it];  // valid slots before slot j
-    const int t = (int)(j / K);
+    const int t = small ? (int)((uint32_t)j / (uint32_t)K) : (int)(j / K);
     if (j - (int64_t)t * K == 0) out.tok_off[t] = q;
     const int e = r_e[it];
     if (e < 0) continue;
-    int s = s_before[e] + r_rank[it];
+    int s = s_base[e] + r_rank[it];
     for (int w2 = 0; w2 < w; w2++) s += s_run[w2 * E + e];
-    if (s < cap) {
+    if ((unsigned)s < (unsigned)cap) {
       out.x_gather_idx[s] = t;
       out.s_scatter_idx[s] = q;
     }
-    if (q < cap) {
+    if ((unsigned)q < (unsigned)cap) {
       out.s_reverse_scatter_idx[q] = s;
       out.router_scores[q] = r_w[it];
     }
   }
 }
 
-hipError_t launch_meta_hist(const int32_t *topk_idx, int N, int K, int E, int32_t *hist_ws,
+hipError_t launch_meta_hist(const int32_t *topk_idx, int N, int K, int E, int32_t *ws,
                             hipStream_t stream) {
   const int64_t NK = (int64_t)N * K;
-  hipLaunchKernelGGL(meta_hist_kernel, dim3(meta_blocks(NK)), dim3(kMetaThreads),
-                     (size_t)(E + 1) * sizeof(int32_t), stream, topk_idx, NK, E, hist_ws);
+  const MetaWs L = meta_ws_layout(NK, E);
+  hipLaunchKernelGGL(meta_hist_kernel, dim3(L.nblk), dim3(kMetaThreads),
+                     (size_t)(E + 2) * sizeof(int32_t), stream, topk_idx, NK, E, ws + L.hist);
+  return hipGetLastError();
+}
+
+hipError_t launch_meta_scan(int N, int K, int E, int32_t *ws, hipStream_t stream) {
+  const MetaWs L = meta_ws_layout((int64_t)N * K, E);
+  hipLaunchKernelGGL(meta_scan_kernel, dim3(E + 2), dim3(kMetaThreads), 0, stream, ws + L.hist,
+                     E + 2, L.nblk, ws + L.pre, ws + L.tot);
   return hipGetLastError();
 }
 
 hipError_t launch_meta_scatter(const int32_t *topk_idx, const float *topk_weights, int N, int K,
-                               int E, int capacity, const int32_t *hist_ws, const MetaOut &out,
+                               int E, int capacity, const int32_t *ws, const MetaOut &out,
                                hipStream_t stream) {
-  const int nblk = meta_blocks((int64_t)N * K);
+  const MetaWs L = meta_ws_layout((int64_t)N * K, E);
   int nbits = 0;
   while ((1 << nbits) < E) nbits++;
-  const size_t sh = (size_t)(2 * E + 3 + 4 * E + 8) * sizeof(int32_t);
-  hipLaunchKernelGGL(meta_scatter_kernel, dim3(nblk), dim3(kMetaThreads), sh, stream, topk_idx,
-                     topk_weights, N, K, E, nbits, nblk, capacity, hist_ws, out);
+  const size_t sh = (size_t)(2 * (E + 2) + 4 * E + 8) * sizeof(int32_t);
+  hipLaunchKernelGGL(meta_scatter_kernel, dim3(L.nblk), dim3(kMetaThreads), sh, stream, topk_idx,
+                     topk_weights, N, K, E, nbits, capacity, ws + L.pre, ws + L.tot, out);
   return hipGetLastError();
 }
 
