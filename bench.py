@@ -101,6 +101,49 @@ def cpu_baseline(d, backward: bool, target_s: float):
     }
 
 
+def metadata_sweep(moe, synth, torch, np):
+    """Metadata build alone over N = 2^14..2^20 at K=8, E=64: device time of 20 builds
+    captured in one HIP graph, and the algorithmic bytes over that time."""
+    dev = torch.device("cuda:0")
+    K, E, reps = 8, 64, 20
+    rows = []
+    for logn in range(14, 21):
+        N = 1 << logn
+        idx_np = synth.routing_uniform(N, E, K, p_invalid=0.2, min_valid=0, seed=logn)
+        w_np = synth.make_topk_weights(idx_np, logn)
+        P = int((idx_np >= 0).sum())
+        idx = torch.from_numpy(idx_np).to(dev)
+        w = torch.from_numpy(w_np).to(dev)
+        meta = moe.Metadata(N, K, E, P, device=dev)
+        ws = torch.empty(max(1, moe.moe_build_metadata_workspace(N, K, E)), dtype=torch.uint8,
+                         device=dev)
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            moe.moe_build_metadata(idx, w, meta, workspace=ws)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cs):
+            for _ in range(reps):
+                moe.moe_build_metadata(idx, w, meta, workspace=ws)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        assert int(meta.status.item()) == 0
+        us = 1e3 * e0.elapsed_time(e1) / reps
+        nbytes = 8 * N * K + 16 * P + 4 * (N + 1) + 4 * E + 4 * (E + 1)
+        rows.append({"N": N, "P": P, "us": round(us, 2), "bytes": nbytes,
+                     "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                     "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)})
+        print(json.dumps(rows[-1]), flush=True)
+    print(json.dumps({"metric": "metadata build time and HBM fraction, K=8 E=64",
+                      "unit": "us", "sweep": rows}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,6 +153,11 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cold-reps", type=int, default=5,
+                    help="single steps timed after a 1 GiB fill evicts L2 and the MALL")
+    ap.add_argument("--metadata-sweep", action="store_true",
+                    help="instead of the benchmark, time the metadata build alone for "
+                         "N = 2^14 .. 2^20 rows at K=8, E=64 (uniform routing, 20%% -1 slots)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the benchmark, run a plain device copy of this many MiB "
                          "(reference kernel for scaling HBM traffic counters)")
@@ -134,6 +182,10 @@ def main():
 
     import synth
     import token_routing_grouped_amd as moe
+
+    if args.metadata_sweep:
+        metadata_sweep(moe, synth, torch, np)
+        return
 
     cfg = synth.CONFIGS[args.workload]
     backward = cfg["backward"]
@@ -244,6 +296,20 @@ def main():
     dom_ms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)) / args.steps
     assert int(meta.status.item()) == 0
 
+    # cold: each single step follows a 1 GiB fill that evicts L2 and the 256 MB MALL
+    cold = []
+    if args.cold_reps > 0:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        for _ in range(args.cold_reps):
+            flush.zero_()
+            s0.record(stream)
+            step()
+            s1.record(stream)
+            torch.cuda.synchronize()
+            cold.append(s0.elapsed_time(s1))
+        del flush
+        cold.sort()
+
     flops_step = (18 if backward else 6) * P * H * I
     tflops = flops_step / (ms * 1e-3) / 1e12
     dom_flops = GEMM_FLOPS[dominant] * P * H * I
@@ -268,6 +334,9 @@ def main():
                    "step": "metadata + forward" + (" + backward" if backward else ""),
                    "flops_per_step": flops_step},
         "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "cold": ({"ms_per_step": round(cold[len(cold) // 2], 4),
+                  "TFLOPs": round(flops_step / (cold[len(cold) // 2] * 1e-3) / 1e12, 2),
+                  "reps": len(cold)} if cold else None),
         "metadata": {"us": round(meta_us, 2), "eager_us": round(meta_eager_us, 2),
                      "bytes": meta_bytes,
                      "GBps": round(meta_bytes / (meta_us * 1e-6) / 1e9, 1),

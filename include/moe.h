@@ -61,7 +61,14 @@ typedef enum {
 /* Column order of W_up's 2I output columns. The Hysen Labs page on
  * Dao-AILab/sonic-moe ("Interleaved by default, concatenated if your model is
  * HuggingFace") gives the interleaved order gate0, up0, gate1, up1, ... */
-typedef enum { MOE_GATEUP_INTERLEAVED = 0 } moe_gateup_layout;
+/* Column order of W_up [E,H,2I] (and of dW_up):
+ *  INTERLEAVED: column 2j = gate_j, 2j+1 = up_j (the Hysen Labs page on SonicMoE: the
+ *               interleaved format is the default);
+ *  CONCAT:      columns [0,I) = gates, [I,2I) = ups (the concatenated gate/up format of
+ *               HF-style checkpoints that page contrasts it with).
+ * The saved activation h_save is always stored interleaved: it is written by the
+ * forward and read only by the backward of this library. */
+typedef enum { MOE_GATEUP_INTERLEAVED = 0, MOE_GATEUP_CONCAT = 1 } moe_gateup_layout;
 
 /* Device status bits, OR-ed into *meta->status (zeroed by moe_build_metadata). */
 enum { MOE_DEV_BAD_EXPERT = 1u, MOE_DEV_OVER_CAPACITY = 2u };

@@ -14,6 +14,21 @@ import synth
 TOL = {"bf16": 2e-2, "fp32": 1e-4}
 
 
+def gateup_to_concat(w: np.ndarray) -> np.ndarray:
+    """W_up columns (last axis) from interleaved (gate_j, up_j at 2j, 2j+1) to
+    concatenated [gates | ups] order."""
+    return np.concatenate([w[..., 0::2], w[..., 1::2]], axis=-1)
+
+
+def gateup_to_interleaved(w: np.ndarray) -> np.ndarray:
+    """Inverse of gateup_to_concat."""
+    I = w.shape[-1] // 2
+    out = np.empty_like(w)
+    out[..., 0::2] = w[..., :I]
+    out[..., 1::2] = w[..., I:]
+    return out
+
+
 def f64(bits: np.ndarray) -> np.ndarray:
     return synth.bf16_bits_to_f32(bits).astype(np.float64)
 
@@ -35,7 +50,7 @@ def assert_close(got, ref, tol, name=""):
 class Gpu:
     """One case's inputs on the device, in bf16 or fp32 storage."""
 
-    def __init__(self, d: dict, dtype: str = "bf16", capacity=None, device="cuda"):
+    def __init__(self, d: dict, dtype: str = "bf16", capacity=None, device="cuda", layout=0):
         import torch
         from token_routing_grouped_amd import Metadata
 
@@ -50,8 +65,9 @@ class Gpu:
             t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
             return t.to(device).to(tdt).contiguous()
 
+        self.layout = layout  # 1: W_up (and dW_up) in concatenated [gates | ups] order
         self.x = dev(d["x"])
-        self.w_up = dev(d["w_up"])
+        self.w_up = dev(gateup_to_concat(d["w_up"]) if layout == 1 else d["w_up"])
         self.w_down = dev(d["w_down"])
         self.dout = dev(d["dout"]) if "dout" in d else None
         self.topk_idx = torch.from_numpy(d["topk_idx"]).to(device)
@@ -72,7 +88,8 @@ class Gpu:
         self.out = torch.empty(self.N, self.H, dtype=self.tdt, device=self.x.device)
         self.h = (torch.empty(max(self.meta.capacity, 0), 2 * self.I, dtype=self.tdt,
                               device=self.x.device) if save_h else None)
-        moe_expert_forward(self.meta, self.x, self.w_up, self.w_down, self.out, h_save=self.h)
+        moe_expert_forward(self.meta, self.x, self.w_up, self.w_down, self.out, h_save=self.h,
+                           layout=self.layout)
         return self.out
 
     def backward(self):
@@ -84,7 +101,8 @@ class Gpu:
         self.dw_down = torch.empty(self.E, self.I, self.H, dtype=self.tdt, device=dev)
         self.dtw = torch.empty(self.N, self.K, dtype=torch.float32, device=dev)
         moe_expert_backward(self.meta, self.topk_idx, self.x, self.w_up, self.w_down, self.h,
-                            self.dout, self.dx, self.dw_up, self.dw_down, self.dtw)
+                            self.dout, self.dx, self.dw_up, self.dw_down, self.dtw,
+                            layout=self.layout)
 
     def meta_numpy(self) -> dict:
         m = self.meta

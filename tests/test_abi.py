@@ -50,8 +50,8 @@ def test_synchronous_argument_errors():
                                 1 << 30, None) == 3
     assert L.moe_expert_forward(ctypes.byref(m), 16, 16, 16, 128, 128, 7, 0, None, 16, 16,
                                 1 << 30, None) == 3
-    assert L.moe_expert_forward(ctypes.byref(m), 16, 16, 16, 128, 128, 0, 1, None, 16, 16,
-                                1 << 30, None) == 3
+    assert L.moe_expert_forward(ctypes.byref(m), 16, 16, 16, 128, 128, 0, 2, None, 16, 16,
+                                1 << 30, None) == 3  # no gate/up layout 2
     # short forward / backward workspace
     fneed = L.moe_expert_forward_workspace(ctypes.byref(m), 128, 128, 0)
     assert L.moe_expert_forward(ctypes.byref(m), 16, 16, 16, 128, 128, 0, 0, None, 16, 16,

@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import synth
-from _util import TOL, Gpu, assert_close, f64, np64
+from _util import TOL, Gpu, assert_close, f64, gateup_to_concat, np64
 
 pytestmark = pytest.mark.gpu
 
@@ -149,3 +149,31 @@ def test_n_zero():
     g.forward()
     g.backward()
     assert np.all(np64(g.dw_up) == 0) and np.all(np64(g.dw_down) == 0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_concat_gate_up_layout(dtype):
+    """W_up stored [gates | ups] (MOE_GATEUP_CONCAT): the same layer as the interleaved
+    storage of the same weights (the Hysen Labs page on SonicMoE, gate/up formats).
+    Against the oracle, with dW_up compared in the concatenated order; against the
+    interleaved run, the up-projection tiles hold the same values, so the forward and
+    every gradient except dx (whose 2I contraction runs in another order) match bit for bit."""
+    d = synth.case(N=600, H=384, I=256, E=5, K=4, seed=21, p_invalid=0.3)
+    print(f"concat layout case dtype={dtype}", flush=True)
+    m, f, gr = oracle_full(d)
+    gi = Gpu(d, dtype=dtype)
+    gc = Gpu(d, dtype=dtype, layout=1)
+    for g in (gi, gc):
+        g.build()
+        g.forward()
+        g.backward()
+    tol = TOL[dtype]
+    assert_close(np64(gc.out), f["out"], tol, "out")
+    assert_close(np64(gc.h)[:m["P"]], f["h"], tol, "h_save (interleaved)")
+    assert_close(np64(gc.dx), gr["dx"], tol, "dx")
+    assert_close(np64(gc.dw_up), gateup_to_concat(gr["dw_up"]), tol, "dw_up (concat)")
+    assert_close(np64(gc.dw_down), gr["dw_down"], tol, "dw_down")
+    assert_close(gc.dtw.cpu().numpy().astype(np.float64), gr["d_topk_weights"], tol, "dtw")
+    for a, b in [(gi.out, gc.out), (gi.h, gc.h), (gi.dw_down, gc.dw_down), (gi.dtw, gc.dtw)]:
+        assert np.array_equal(np64(a), np64(b))
+    assert np.array_equal(gateup_to_concat(np64(gi.dw_up)), np64(gc.dw_up))

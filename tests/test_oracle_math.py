@@ -205,3 +205,26 @@ def test_sampled_entry_points_match_full():
     st32 = oracle.sample_tokens(x.astype(np.float32), wu.astype(np.float32),
                                 wd.astype(np.float32), idx, w, toks)
     assert relerr(st32["out"], f["out"]) < 1e-12
+
+
+def test_concat_gate_up_reading():
+    """The concatenated W_up layout means columns [0,I) are the gates and [I,2I) the
+    ups (the Hysen Labs page on SonicMoE contrasts it with the interleaved default).
+    With E=1, K=1 and unit weights the layer is a dense SwiGLU MLP; written out in
+    numpy on W_up = [W_gate | W_up] it must equal the oracle fed the same weights
+    reordered to interleaved columns by the test helper."""
+    from _util import gateup_to_concat, gateup_to_interleaved
+    rng = np.random.default_rng(31)
+    N, H, I = 9, 12, 5
+    x = rng.standard_normal((N, H))
+    w_cat = rng.standard_normal((1, H, 2 * I)) * 0.3
+    w_down = rng.standard_normal((1, I, H)) * 0.3
+    g, u = x @ w_cat[0][:, :I], x @ w_cat[0][:, I:]
+    want = (g / (1.0 + np.exp(-g)) * u) @ w_down[0]
+    idx = np.zeros((N, 1), np.int32)
+    m = oracle.build_metadata(idx, np.ones((N, 1), np.float32), 1)
+    got = oracle.forward(x, gateup_to_interleaved(w_cat), w_down, m)["out"]
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+    w = rng.standard_normal((3, 4, 2 * I))
+    assert np.array_equal(gateup_to_interleaved(gateup_to_concat(w)), w)
+    assert np.array_equal(gateup_to_concat(w)[..., :I], w[..., 0::2])

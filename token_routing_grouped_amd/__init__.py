@@ -6,7 +6,7 @@ provides device memory and the stream. There is no fallback: if the library is
 not built, importing the binding raises.
 """
 from ._binding import (  # noqa: F401
-    MOE_BF16, MOE_FP32, MOE_GATEUP_INTERLEAVED, MOE_DEV_BAD_EXPERT, MOE_DEV_OVER_CAPACITY,
+    MOE_BF16, MOE_FP32, MOE_GATEUP_INTERLEAVED, MOE_GATEUP_CONCAT, MOE_DEV_BAD_EXPERT, MOE_DEV_OVER_CAPACITY,
     MoeError, Metadata, lib, moe_build_metadata, moe_build_metadata_workspace,
     moe_expert_forward, moe_expert_forward_workspace, moe_expert_backward,
     moe_expert_backward_workspace, moe_status_string, EXPORTED_SYMBOLS, KERNELS,

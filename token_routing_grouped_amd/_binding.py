@@ -16,6 +16,7 @@ _SO = os.path.join(_HERE, "libmoe.so")
 MOE_OK, MOE_EINVAL, MOE_ENOSPC, MOE_EUNSUPPORTED, MOE_EHIP = range(5)
 MOE_BF16, MOE_FP32 = 0, 1
 MOE_GATEUP_INTERLEAVED = 0
+MOE_GATEUP_CONCAT = 1
 MOE_DEV_BAD_EXPERT, MOE_DEV_OVER_CAPACITY = 1, 2
 
 EXPORTED_SYMBOLS = [

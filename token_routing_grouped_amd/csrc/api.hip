@@ -162,7 +162,7 @@ moe_status moe_expert_forward(const moe_metadata *meta, const void *x, const voi
                               void *workspace, size_t workspace_bytes, void *stream) {
   if (!meta_ok(meta)) return MOE_EINVAL;
   if (dt != MOE_BF16 && dt != MOE_FP32) return MOE_EUNSUPPORTED;
-  if (layout != MOE_GATEUP_INTERLEAVED) return MOE_EUNSUPPORTED;
+  if (layout != MOE_GATEUP_INTERLEAVED && layout != MOE_GATEUP_CONCAT) return MOE_EUNSUPPORTED;
   if (!dims_ok(H, I)) return MOE_EUNSUPPORTED;
   if (meta->N > 0 && (!x || !w_up || !w_down || !out)) return MOE_EINVAL;
   const FwdWs L = fwd_layout(meta, H, I, dt);
@@ -186,6 +186,7 @@ moe_status moe_expert_forward(const moe_metadata *meta, const void *x, const voi
   g.ldc = 2 * I;
   g.C2 = a;
   g.ldc2 = I;
+  g.gu_concat = layout == MOE_GATEUP_CONCAT;
   moe_status s = gemm(kUpSwiGLU, MOE_KERNEL_UP_SWIGLU, g, dt, st);
   if (s != MOE_OK) return s;
   // y = a W_down
@@ -217,7 +218,7 @@ moe_status moe_expert_backward(const moe_metadata *meta, const int32_t *topk_idx
                                size_t workspace_bytes, void *stream) {
   if (!meta_ok(meta)) return MOE_EINVAL;
   if (dt != MOE_BF16 && dt != MOE_FP32) return MOE_EUNSUPPORTED;
-  if (layout != MOE_GATEUP_INTERLEAVED) return MOE_EUNSUPPORTED;
+  if (layout != MOE_GATEUP_INTERLEAVED && layout != MOE_GATEUP_CONCAT) return MOE_EUNSUPPORTED;
   if (!dims_ok(H, I)) return MOE_EUNSUPPORTED;
   if (!w_up || !w_down || !dw_up || !dw_down) return MOE_EINVAL;
   if (meta->N > 0 && (!topk_idx || !x || !dout || !dx || !d_topk_weights)) return MOE_EINVAL;
@@ -248,6 +249,7 @@ moe_status moe_expert_backward(const moe_metadata *meta, const int32_t *topk_idx
   g.scores = meta->router_scores;
   g.s_scatter = meta->s_scatter_idx;
   g.partial = partial;
+  g.gu_concat = layout == MOE_GATEUP_CONCAT;  // dh takes W_up's column order
   if (dt == MOE_BF16) {  // one dscore partial per column tile of this GEMM
     int bm, bn, bk;
     gemm_tile(kDownBwd, g, &bm, &bn, &bk);

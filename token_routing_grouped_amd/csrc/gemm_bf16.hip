@@ -38,7 +38,8 @@ constexpr int PADK = 8;   // extra elements per row of a reduction-contiguous ti
 constexpr int PADC = 32;  // extra columns of an M/N-contiguous tile [BK][cols]
 
 enum { GROUPED_M = 0, VARLEN_K = 1 };
-enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_DSWIGLU = 2 };
+// EPI_SWIGLU: W_up interleaved (gate_j, up_j at 2j, 2j+1); EPI_SWIGLU_CAT: [gates | ups]
+enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_DSWIGLU = 2, EPI_SWIGLU_CAT = 3 };
 
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 
@@ -76,7 +77,8 @@ void gemm_bf16_kernel(GemmArgs g) {
   constexpr int NT = 64 * WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;  // wave tile
   constexpr int TM = WM / 32, TN = WN / 32;    // 32x32 sub-tiles per wave
-  static_assert(TM >= 1 && TN >= 1 && (EPI != EPI_SWIGLU || TN % 2 == 0), "wave tile");
+  constexpr bool SWI = EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_CAT;
+  static_assert(TM >= 1 && TN >= 1 && (!SWI || TN % 2 == 0), "wave tile");
   using AS = TileShape<A_KC, BM, BK>;
   using BS = TileShape<B_KC, BN, BK>;
   constexpr int CPK = BK / 8;  // 16-byte chunks per row of a reduction-contiguous tile
@@ -179,8 +181,16 @@ void gemm_bf16_kernel(GemmArgs g) {
       } else {
         constexpr int CPR = BN / 8;  // chunks per k-row
         const int kr = tid / CPR + (NT / CPR) * i;
-        b_ptr[i] = B + (int64_t)e * g.b_es + (int64_t)kr * g.ldb + (int64_t)nt * BN +
-                   (tid % CPR) * 8;
+        int64_t col = (int64_t)nt * BN + (tid % CPR) * 8;
+        if constexpr (EPI == EPI_SWIGLU_CAT) {
+          // LDS chunk -> the gate or up columns it holds in the per-wave [gates | ups]
+          // order the SwiGLU epilogue reads (see the stage store of EPI_SWIGLU)
+          static_assert((WN / 2) % 8 == 0, "gate/up halves in whole chunks");
+          const int c = (tid % CPR) * 8, w = c / WN, cw = c % WN;
+          const int jb = nt * (BN / 2) + w * (WN / 2);
+          col = cw < WN / 2 ? jb + cw : g.N / 2 + jb + (cw - WN / 2);
+        }
+        b_ptr[i] = B + (int64_t)e * g.b_es + (int64_t)kr * g.ldb + col;
       }
     }
   }
@@ -399,8 +409,8 @@ void gemm_bf16_kernel(GemmArgs g) {
       }
       *(u32x4 *)(C + off + (int64_t)nt * BN + ch * 8) = *(const u32x4 *)(Cs + row * CLD + ch * 8);
     }
-  } else if constexpr (EPI == EPI_SWIGLU) {
-    uint16_t *Hs = (uint16_t *)g.C;  // may be null (inference)
+  } else if constexpr (SWI) {
+    uint16_t *Hs = (uint16_t *)g.C;  // may be null (inference); always interleaved
     uint16_t *Aout = (uint16_t *)g.C2;
 #pragma unroll
     for (int mi = 0; mi < TM; mi++)
@@ -468,7 +478,12 @@ void gemm_bf16_kernel(GemmArgs g) {
           const float dg = da * up * sg * (1.0f + gt * (1.0f - sg));
           const float du = da * gt * sg;
           if (ok) {
-            *(uint32_t *)(dH + srow[r] * g.ldc + 2 * j) = pack_bf16x2(dg, du);
+            if (g.gu_concat) {  // dh in W_up's column order
+              dH[srow[r] * g.ldc + j] = f32_to_bf16(dg);
+              dH[srow[r] * g.ldc + g.N + j] = f32_to_bf16(du);
+            } else {
+              *(uint32_t *)(dH + srow[r] * g.ldc + 2 * j) = pack_bf16x2(dg, du);
+            }
             AW[srow[r] * g.ldc2 + j] = f32_to_bf16(wq[r] * a);
           }
         }
@@ -569,6 +584,8 @@ hipError_t launch_gemm_bf16(GemmKind kind, const GemmArgs &g, hipStream_t st) {
   gemm_tile(kind, g, &bm, &bn, &bk);
   switch (kind) {
     case kUpSwiGLU:
+      if (g.gu_concat)
+        return launch_tiles<GROUPED_M, true, false, EPI_SWIGLU_CAT>(bm, bn, bk, grid, g, st);
       return launch_tiles<GROUPED_M, true, false, EPI_SWIGLU>(bm, bn, bk, grid, g, st);
     case kDown:
       return launch_tiles<GROUPED_M, true, false, EPI_STORE>(bm, bn, bk, grid, g, st);

@@ -86,9 +86,17 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(GemmArgs g) {
       for (int i = 0; i < 8; i++) Bs[kk + i][n] = src[i];
     } else if constexpr (MODE == GROUPED_M) {  // weights [K][N]
       const int kr = tid >> 4, n = (tid & 15) * 8;
-      const float *src = B + (int64_t)e * g.b_es + (int64_t)(k0 + kr) * g.ldb + (int64_t)nt * BN + n;
+      const float *row = B + (int64_t)e * g.b_es + (int64_t)(k0 + kr) * g.ldb;
+      if (EPI == EPI_SWIGLU && g.gu_concat) {  // tile column c holds gate/up of pair c/2
 #pragma unroll
-      for (int i = 0; i < 8; i++) Bs[kr][n + i] = src[i];
+        for (int i = 0; i < 8; i++) {
+          const int c = nt * BN + n + i;
+          Bs[kr][n + i] = row[(c & 1) ? g.N / 2 + (c >> 1) : (c >> 1)];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; i++) Bs[kr][n + i] = row[(int64_t)nt * BN + n + i];
+      }
     } else {
       const int kr = tid >> 4, n = (tid & 15) * 8;
       const int kk = k0 + kr;
@@ -168,8 +176,9 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(GemmArgs g) {
           const float a = gt * sg * up;
           part += dau * a;
           const float da = wq * dau;
-          dH[s * g.ldc + 2 * j] = da * up * sg * (1.0f + gt * (1.0f - sg));
-          dH[s * g.ldc + 2 * j + 1] = da * gt * sg;
+          const int64_t cg = g.gu_concat ? j : 2 * j, cu = g.gu_concat ? g.N + j : 2 * j + 1;
+          dH[s * g.ldc + cg] = da * up * sg * (1.0f + gt * (1.0f - sg));
+          dH[s * g.ldc + cu] = da * gt * sg;
           AW[s * g.ldc2 + j] = wq * a;
         }
       }

@@ -84,6 +84,7 @@ struct GemmArgs {
   const int32_t *s_scatter;  // s -> q
   float *partial;            // kDownBwd: [cap, n_ntiles] per-tile partial dscore
   int n_ntiles;
+  int gu_concat;  // kUpSwiGLU / kDownBwd: W_up (and dh) columns are [gates | ups]
 };
 
 constexpr int kGemmBM = 128, kGemmBN = 128, kGemmBK = 64;  // smallest tile; fp32 mode tile
