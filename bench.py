@@ -144,6 +144,47 @@ def metadata_sweep(moe, synth, torch, np):
                       "unit": "us", "sweep": rows}), flush=True)
 
 
+def router_timing(moe, synth, torch, np, N=32768, E=128, K=8, reps=20):
+    """moe_route (top-K + weights + aux loss + the metadata) alone, at the routing
+    example of the Hysen Labs page (32768 tokens, 128 experts, top-8, fp32 logits):
+    device time of reps calls captured in one HIP graph, algorithmic bytes over it."""
+    dev = torch.device("cuda:0")
+    lg = torch.from_numpy(synth.router_logits(N, E, seed=1)).to(dev)
+    meta = moe.Metadata(N, K, E, N * K, device=dev)
+    idx = torch.empty(N, K, dtype=torch.int32, device=dev)
+    w = torch.empty(N, K, dtype=torch.float32, device=dev)
+    aux = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, moe.moe_route_workspace(N, K, E)), dtype=torch.uint8, device=dev)
+
+    def call():
+        moe.moe_route(lg, meta, mode=moe.MOE_ROUTE_TOPK_SOFTMAX, renormalize=True, topk_idx=idx,
+                      topk_weights=w, aux_loss=aux, workspace=ws)
+
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cs):
+        for _ in range(reps):
+            call()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / reps
+    P = N * K
+    # logits read; topk_idx/weights written then re-read by the scatter; metadata written
+    nbytes = 4 * N * E + 8 * N * K * 2 + 16 * P + 4 * (N + 1) + 4 * E + 4 * (E + 1)
+    return {"N": N, "E": E, "K": K, "mode": "topk_of_softmax+renorm", "us": round(us, 2),
+            "bytes": nbytes, "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -235,7 +276,9 @@ def main():
     assert torch.isfinite(out.float()).all()
 
     # per-kernel durations (3 launches each) to name the dominant kernel
-    kernels = moe.KERNELS if backward else moe.KERNELS[:moe.KERNELS.index("combine") + 1]
+    # the kernels one step launches (the router is timed on its own below)
+    step_kernels = [k for k in moe.KERNELS if not k.startswith("route")]
+    kernels = step_kernels if backward else step_kernels[:step_kernels.index("combine") + 1]
     kernel_us = {}
     for k in kernels:
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
@@ -349,6 +392,7 @@ def main():
                      "flops_per_launch": dom_flops},
         "wall_s_timed": round(wall, 4),
     }
+    res["router"] = router_timing(moe, synth, torch, np)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(d, backward, args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -98,6 +98,7 @@ typedef struct {
 
 /* Workspace byte counts. Zero means no workspace is needed. */
 size_t moe_build_metadata_workspace(int32_t N, int32_t K, int32_t E);
+size_t moe_route_workspace(int32_t N, int32_t K, int32_t E);
 size_t moe_expert_forward_workspace(const moe_metadata *meta, int32_t H, int32_t I,
                                     moe_dtype dt);
 size_t moe_expert_backward_workspace(const moe_metadata *meta, int32_t H, int32_t I,
@@ -114,6 +115,28 @@ size_t moe_expert_backward_workspace(const moe_metadata *meta, int32_t H, int32_
 moe_status moe_build_metadata(const int32_t *topk_idx, const float *topk_weights,
                               const moe_metadata *meta, void *workspace,
                               size_t workspace_bytes, void *stream);
+
+/* Router top-K from logits, fused with the metadata build (the Hysen Labs page on
+ * Dao-AILab/sonic-moe, section "Three routing strategies, selected on the command
+ * line": softmax over the top-K logits, or top-K over the softmax of all experts with
+ * optional renormalisation; the layer also returns an auxiliary load-balancing loss).
+ *  logits        [N,E] bf16 or fp32 (logits_dtype), N, K, E taken from *meta; K <= E.
+ *  topk_idx      [N,K] int32 out: per token the K experts with the largest logits,
+ *                largest first; equal logits go to the lower expert id.
+ *  topk_weights  [N,K] fp32 out: MOE_ROUTE_SOFTMAX_TOPK: exp(l_k) / sum over the K;
+ *                MOE_ROUTE_TOPK_SOFTMAX: exp(l_k) / sum over all E, divided by the
+ *                sum of the K when renormalize != 0.
+ *  aux_loss      [1] fp32 out or NULL: E * sum_e f_e * P_e, f_e = share of the N*K
+ *                slots routed to e, P_e = mean over tokens of the softmax over all E
+ *                at e (0 when N = 0).
+ *  meta          filled exactly as moe_build_metadata(topk_idx, topk_weights) would.
+ * Device pointers, caller-owned; workspace >= moe_route_workspace(N, K, E). Errors as
+ * for moe_build_metadata (MOE_EINVAL also when K > E); only enqueues on stream. */
+typedef enum { MOE_ROUTE_SOFTMAX_TOPK = 0, MOE_ROUTE_TOPK_SOFTMAX = 1 } moe_route_mode;
+moe_status moe_route(const void *logits, moe_dtype logits_dtype, moe_route_mode mode,
+                     int32_t renormalize, int32_t *topk_idx, float *topk_weights,
+                     float *aux_loss, const moe_metadata *meta, void *workspace,
+                     size_t workspace_bytes, void *stream);
 
 /* Forward (issue #68 dataflow: native non-expand metadata + local expert
  * compute -> local_out [N_recv,H]). For sorted position s of expert e, token t:
@@ -162,7 +185,10 @@ typedef enum {
   MOE_KERNEL_WGRAD_UP = 9,     /* backward: dW_up */
   MOE_KERNEL_COMBINE_DX = 10,  /* backward: dx = sum over the token's rows, and
                                   d_topk_weights in [N,K] */
-  MOE_KERNEL_COUNT = 11
+  MOE_KERNEL_ROUTE = 11,       /* moe_route: top-K, weights, histograms, P sums
+                                  (then META_SCAN and META_SCATTER, which also form the
+                                  load-balancing loss) */
+  MOE_KERNEL_COUNT = 12
 } moe_kernel_id;
 
 /* After this call, the i-th launch of `kernel` (i < n_launches, counted from this

@@ -74,6 +74,8 @@ def _declare(L):
     L.oracle_sample_dw_up_cols.restype = None
     L.oracle_sample_dw_up_cols.argtypes = [_i64] * 3 + [_vp, _int, _vp, _int, _vp, _vp, _int,
                                                         _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp]
+    L.oracle_route.restype = None
+    L.oracle_route.argtypes = [_i64] * 3 + [_vp, _int, _int, _int, _vp, _vp, _vp]
     L.oracle_num_threads.restype = _int
     L.oracle_num_threads.argtypes = []
 
@@ -95,6 +97,19 @@ def _typed(a: np.ndarray):
     if a.dtype == np.float64:
         return a, F64
     raise TypeError(f"unsupported oracle tensor dtype {a.dtype}")
+
+
+def route(logits, K: int, mode: int, renormalize: bool = False) -> dict:
+    """Router top-K, weights and the load-balancing aux loss (see oracle_route).
+    logits [N,E] as bf16 bits (uint16), fp32 or fp64."""
+    lg, dt = _typed(logits)
+    N, E = lg.shape
+    idx = np.zeros((N, K), np.int32)
+    w = np.zeros((N, K), np.float64)
+    aux = np.zeros(1, np.float64)
+    lib().oracle_route(N, E, K, _p(lg), dt, int(mode), int(bool(renormalize)), _p(idx), _p(w),
+                       _p(aux))
+    return dict(topk_idx=idx, topk_weights=w, aux=float(aux[0]))
 
 
 def num_threads() -> int:

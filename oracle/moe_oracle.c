@@ -517,3 +517,51 @@ void oracle_sample_dw_up_cols(int64_t H, int64_t I, int64_t E,
         free(xrow);
     }
 }
+
+/* Router: see the header. One token at a time; selection by repeated strict maxima
+ * over the experts not yet taken, scanning e upward (so equal logits go to the lower
+ * id); probabilities and the aux sums in fp64. */
+void oracle_route(int64_t N, int64_t E, int64_t K, const void *logits, int logits_dt, int mode,
+                  int renormalize, int32_t *topk_idx, double *topk_weights, double *aux) {
+    double *l = (double *)malloc(sizeof(double) * (size_t)(E > 0 ? E : 1));
+    char *taken = (char *)malloc((size_t)(E > 0 ? E : 1));
+    double *count = (double *)calloc((size_t)(E > 0 ? E : 1), sizeof(double));
+    double *psum = (double *)calloc((size_t)(E > 0 ? E : 1), sizeof(double));
+    for (int64_t t = 0; t < N; t++) {
+        for (int64_t e = 0; e < E; e++) {
+            l[e] = ld(logits, logits_dt, t * E + e);
+            taken[e] = 0;
+        }
+        for (int64_t k = 0; k < K; k++) {
+            int64_t best = -1;
+            for (int64_t e = 0; e < E; e++)
+                if (!taken[e] && (best < 0 || l[e] > l[best])) best = e;
+            taken[best] = 1;
+            topk_idx[t * K + k] = (int32_t)best;
+            count[best] += 1.0;
+        }
+        const double mx = l[topk_idx[t * K]];
+        double z_all = 0.0;
+        for (int64_t e = 0; e < E; e++) z_all += exp(l[e] - mx);
+        for (int64_t e = 0; e < E; e++) psum[e] += exp(l[e] - mx) / z_all;
+        double z_sel = 0.0;
+        for (int64_t k = 0; k < K; k++) z_sel += exp(l[topk_idx[t * K + k]] - mx);
+        for (int64_t k = 0; k < K; k++) {
+            const double v = exp(l[topk_idx[t * K + k]] - mx);
+            double wk;
+            if (mode == 0)
+                wk = v / z_sel;
+            else
+                wk = renormalize ? (v / z_all) / (z_sel / z_all) : v / z_all;
+            topk_weights[t * K + k] = wk;
+        }
+    }
+    double a = 0.0;
+    if (N > 0 && K > 0)
+        for (int64_t e = 0; e < E; e++) a += (count[e] / (double)(N * K)) * (psum[e] / (double)N);
+    *aux = (double)E * a;
+    free(l);
+    free(taken);
+    free(count);
+    free(psum);
+}

@@ -132,6 +132,24 @@ void oracle_sample_dw_up_cols(int64_t H, int64_t I, int64_t E,
                               int64_t n, const int64_t *e_list, const int64_t *jj_list,
                               double *cols);
 
+/* Router ahead of the metadata (Hysen Labs page on Dao-AILab/sonic-moe, section
+ * "Three routing strategies, selected on the command line"). Per token t, the K
+ * experts with the largest logits, listed largest first (reading: equal logits go
+ * to the lower expert id), with weights
+ *   mode 0, softmax over the top-K logits:  w_k = exp(l_k) / sum over the K of exp(l);
+ *   mode 1, top-K of the softmax over all E: w_k = exp(l_k) / sum over all E of exp(l),
+ *           divided by the sum of the K selected values when renormalize != 0.
+ * Selecting by logits equals selecting by softmax probabilities (softmax is
+ * increasing); the choice is made exactly on the given values.
+ * aux (reading: the page names the auxiliary load-balancing loss the layer returns,
+ * without a formula; this is the usual load-balancing product form):
+ *   aux = E * sum_e f_e * P_e,  f_e = (slots routed to e) / (N*K),
+ *   P_e = (1/N) * sum_t softmax over all E of logits[t,:], at e.
+ * logits [N,E] typed (ORACLE_BF16 / F32 / F64). Outputs topk_idx [N,K],
+ * topk_weights [N,K] (fp64), *aux (0 when N = 0). */
+void oracle_route(int64_t N, int64_t E, int64_t K, const void *logits, int logits_dt, int mode,
+                  int renormalize, int32_t *topk_idx, double *topk_weights, double *aux);
+
 /* Threads the OpenMP loops use (for the benchmark's CPU-baseline report). */
 int oracle_num_threads(void);
 

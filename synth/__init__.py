@@ -47,7 +47,7 @@ CONFIGS = {
 }
 
 # independent streams per drawn quantity, so changing one draw leaves the others fixed
-_S_ROUTE, _S_LOGIT, _S_X, _S_WUP, _S_WDOWN, _S_DOUT = range(6)
+_S_ROUTE, _S_LOGIT, _S_X, _S_WUP, _S_WDOWN, _S_DOUT, _S_LOGITS = range(7)
 
 
 def _rng(seed: int, stream: int) -> np.random.Generator:
@@ -208,6 +208,16 @@ def make_inputs(name_or_cfg, seed: int = 0, dout: bool = True, topk_idx=None,
     if dout:
         d["dout"] = bf16_normal(used, _S_DOUT, (N, H), 1.0)
     return d
+
+
+def router_logits(N: int, E: int, seed: int, ties: bool = False) -> np.ndarray:
+    """Router logits [N,E] fp32 ~ N(0,1); with ties=True they are rounded to multiples
+    of 0.25 in [-1, 1], so most rows hold many equal values."""
+    rng = _rng(seed, _S_LOGITS)
+    lg = rng.standard_normal((N, E)).astype(np.float32)
+    if ties:
+        lg = np.clip(np.round(lg * 4.0) / 4.0, -1.0, 1.0).astype(np.float32)
+    return lg
 
 
 def case(N, H, I, E, K, seed=0, p_invalid=0.1, min_valid=0, topk_idx=None, dout=True,

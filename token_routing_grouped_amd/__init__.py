@@ -10,5 +10,6 @@ from ._binding import (  # noqa: F401
     MoeError, Metadata, lib, moe_build_metadata, moe_build_metadata_workspace,
     moe_expert_forward, moe_expert_forward_workspace, moe_expert_backward,
     moe_expert_backward_workspace, moe_status_string, EXPORTED_SYMBOLS, KERNELS,
-    moe_time_kernel, moe_kernel_name,
+    moe_time_kernel, moe_kernel_name, moe_route, moe_route_workspace, MOE_ROUTE_SOFTMAX_TOPK,
+    MOE_ROUTE_TOPK_SOFTMAX,
 )

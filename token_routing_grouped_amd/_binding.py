@@ -23,9 +23,11 @@ EXPORTED_SYMBOLS = [
     "moe_build_metadata_workspace", "moe_expert_forward_workspace",
     "moe_expert_backward_workspace", "moe_build_metadata", "moe_expert_forward",
     "moe_expert_backward", "moe_status_string", "moe_time_kernel", "moe_kernel_name",
+    "moe_route_workspace", "moe_route",
 ]
 KERNELS = ["meta_hist", "meta_scan", "meta_scatter", "up_swiglu", "down", "combine", "down_bwd",
-           "wgrad_down", "up_bwd", "wgrad_up", "combine_dx"]
+           "wgrad_down", "up_bwd", "wgrad_up", "combine_dx", "route"]
+MOE_ROUTE_SOFTMAX_TOPK, MOE_ROUTE_TOPK_SOFTMAX = 0, 1
 
 
 class MoeError(RuntimeError):
@@ -72,6 +74,10 @@ def lib():
         L.moe_expert_backward.restype = ctypes.c_int
         L.moe_expert_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, ctypes.c_int,
                                           ctypes.c_int, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_route_workspace.restype = sz
+        L.moe_route_workspace.argtypes = [i32, i32, i32]
+        L.moe_route.restype = ctypes.c_int
+        L.moe_route.argtypes = [vp, ctypes.c_int, ctypes.c_int, i32, vp, vp, vp, vp, vp, sz, vp]
         L.moe_time_kernel.restype = ctypes.c_int
         L.moe_time_kernel.argtypes = [ctypes.c_int, vp, i32, vp]
         L.moe_kernel_name.restype = ctypes.c_char_p
@@ -176,6 +182,35 @@ def moe_build_metadata(topk_idx, topk_weights, meta: Metadata, workspace=None, s
     _check(lib().moe_build_metadata(pi, pw, meta.ptr, ws, nb, _stream(stream)),
            "moe_build_metadata")
     return wst
+
+
+def moe_route_workspace(N: int, K: int, E: int) -> int:
+    return int(lib().moe_route_workspace(N, K, E))
+
+
+def moe_route(logits, meta: Metadata, mode: int = MOE_ROUTE_SOFTMAX_TOPK, renormalize=False,
+              topk_idx=None, topk_weights=None, aux_loss=None, workspace=None, stream=None,
+              want_aux: bool = True):
+    """Router top-K of logits [N,E] (bf16 or fp32) fused with the metadata build into
+    meta. Returns (topk_idx [N,K] int32, topk_weights [N,K] fp32, aux_loss [1] fp32 or
+    None); output tensors may be passed in."""
+    N, K, E = meta.N, meta.K, meta.E
+    dev = logits.device
+    pl = _dev(logits, "logits", logits.dtype, (N, E))
+    if topk_idx is None:
+        topk_idx = torch.empty(N, K, dtype=torch.int32, device=dev)
+    if topk_weights is None:
+        topk_weights = torch.empty(N, K, dtype=torch.float32, device=dev)
+    if aux_loss is None and want_aux:
+        aux_loss = torch.empty(1, dtype=torch.float32, device=dev)
+    pi = _dev(topk_idx, "topk_idx", torch.int32, (N, K))
+    pw = _dev(topk_weights, "topk_weights", torch.float32, (N, K))
+    pa = None if aux_loss is None else _dev(aux_loss, "aux_loss", torch.float32, (1,))
+    need = moe_route_workspace(N, K, E)
+    wst, ws, nb = _workspace(workspace, need, dev, stream)
+    _check(lib().moe_route(pl, _dtype_code(logits), int(mode), int(bool(renormalize)), pi, pw,
+                           pa, meta.ptr, ws, nb, _stream(stream)), "moe_route")
+    return topk_idx, topk_weights, aux_loss
 
 
 def moe_expert_forward(meta: Metadata, x, w_up, w_down, out, h_save=None, workspace=None,

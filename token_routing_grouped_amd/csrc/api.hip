@@ -102,6 +102,21 @@ moe_status gemm(GemmKind kind, moe_kernel_id id, const GemmArgs &g, moe_dtype dt
 
 }  // namespace
 
+namespace moe {
+static MetaOut meta_out(const moe_metadata *meta) {
+  MetaOut o;
+  o.expert_frequency = meta->expert_frequency;
+  o.expert_frequency_offset = meta->expert_frequency_offset;
+  o.x_gather_idx = meta->x_gather_idx;
+  o.s_scatter_idx = meta->s_scatter_idx;
+  o.s_reverse_scatter_idx = meta->s_reverse_scatter_idx;
+  o.tok_off = meta->num_activated_expert_per_token_offset;
+  o.router_scores = meta->router_scores;
+  o.status = meta->status;
+  return o;
+}
+}  // namespace moe
+
 extern "C" {
 
 size_t moe_build_metadata_workspace(int32_t N, int32_t K, int32_t E) {
@@ -129,15 +144,7 @@ moe_status moe_build_metadata(const int32_t *topk_idx, const float *topk_weights
   if (NK > 0 && (!topk_idx || !topk_weights)) return MOE_EINVAL;
   const size_t need = meta_workspace_bytes(NK, meta->E);
   if (workspace_bytes < need || !workspace) return MOE_ENOSPC;
-  MetaOut o;
-  o.expert_frequency = meta->expert_frequency;
-  o.expert_frequency_offset = meta->expert_frequency_offset;
-  o.x_gather_idx = meta->x_gather_idx;
-  o.s_scatter_idx = meta->s_scatter_idx;
-  o.s_reverse_scatter_idx = meta->s_reverse_scatter_idx;
-  o.tok_off = meta->num_activated_expert_per_token_offset;
-  o.router_scores = meta->router_scores;
-  o.status = meta->status;
+  const MetaOut o = meta_out(meta);
   hipStream_t st = (hipStream_t)stream;
   hipError_t err;
   {
@@ -153,6 +160,55 @@ moe_status moe_build_metadata(const int32_t *topk_idx, const float *topk_weights
   Bracket b(MOE_KERNEL_META_SCATTER, st);
   err = launch_meta_scatter(topk_idx, topk_weights, meta->N, meta->K, meta->E, meta->capacity,
                             (const int32_t *)workspace, o, st);
+  return err == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+size_t moe_route_workspace(int32_t N, int32_t K, int32_t E) {
+  if (N < 0 || K < 1 || E < 1) return 0;
+  const int64_t NK = (int64_t)N * K;
+  return align_up(meta_workspace_bytes(NK, E)) + route_ws_floats(NK, E) * sizeof(float);
+}
+
+moe_status moe_route(const void *logits, moe_dtype logits_dtype, moe_route_mode mode,
+                     int32_t renormalize, int32_t *topk_idx, float *topk_weights,
+                     float *aux_loss, const moe_metadata *meta, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+  if (!meta_ok(meta)) return MOE_EINVAL;
+  if (logits_dtype != MOE_BF16 && logits_dtype != MOE_FP32) return MOE_EUNSUPPORTED;
+  if (mode != MOE_ROUTE_SOFTMAX_TOPK && mode != MOE_ROUTE_TOPK_SOFTMAX) return MOE_EUNSUPPORTED;
+  if (meta->K > meta->E) return MOE_EINVAL;
+  const int N = meta->N, K = meta->K, E = meta->E;
+  const int64_t NK = (int64_t)N * K;
+  if (NK > 0 && (!logits || !topk_idx || !topk_weights)) return MOE_EINVAL;
+  const size_t need = moe_route_workspace(N, K, E);
+  if (workspace_bytes < need || !workspace) return MOE_ENOSPC;
+  int32_t *mws = (int32_t *)workspace;
+  float *ppart = (float *)((char *)workspace + align_up(meta_workspace_bytes(NK, E)));
+  float *psum = ppart + (size_t)meta_blocks(NK) * E;  // [E] after the [E][nblk] columns
+  MetaOut o = meta_out(meta);
+  const bool want_p = aux_loss != nullptr && N > 0;
+  if (aux_loss) {
+    o.aux = aux_loss;
+    o.psum = want_p ? psum : nullptr;  // N = 0: the loss is 0
+    o.aux_scale = want_p ? (float)((double)E / ((double)N * (double)K * (double)N)) : 0.0f;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t err;
+  {
+    Bracket b(MOE_KERNEL_ROUTE, st);
+    err = N > 0 ? launch_route_hist(logits, logits_dtype == MOE_BF16, N, E, K, (int)mode,
+                                    renormalize != 0, want_p, topk_idx, topk_weights, mws,
+                                    ppart, st)
+                : launch_meta_hist(topk_idx, N, K, E, mws, st);  // empty histogram
+  }
+  if (err != hipSuccess) return MOE_EHIP;
+  {
+    Bracket b(MOE_KERNEL_META_SCAN, st);
+    err = launch_meta_scan(N, K, E, mws, st, want_p ? ppart : nullptr, psum);
+  }
+  if (err != hipSuccess) return MOE_EHIP;
+  Bracket b(MOE_KERNEL_META_SCATTER, st);
+  err = launch_meta_scatter(topk_idx, topk_weights, N, K, E, meta->capacity, mws, o, st);
   return err == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
@@ -325,7 +381,7 @@ moe_status moe_time_kernel(moe_kernel_id kernel, void *const *events, int32_t n_
 const char *moe_kernel_name(moe_kernel_id k) {
   static const char *names[MOE_KERNEL_COUNT] = {
       "meta_hist", "meta_scan", "meta_scatter", "up_swiglu", "down", "combine", "down_bwd",
-      "wgrad_down", "up_bwd", "wgrad_up", "combine_dx"};
+      "wgrad_down", "up_bwd", "wgrad_up", "combine_dx", "route"};
   return ((int)k >= 0 && (int)k < MOE_KERNEL_COUNT) ? names[(int)k] : "unknown";
 }
 

@@ -53,6 +53,21 @@ __device__ __forceinline__ int wave_inclusive_scan_dpp(int v) {
   return v;
 }
 
+// Sum across the 64 lanes of a wave with the same DPP pattern (fixed association
+// order, so deterministic); every lane receives lane 63's total. All lanes active.
+__device__ __forceinline__ float wave_sum_dpp_f32(float v) {
+#define MOE_DPP_ADD(C, R, B) \
+  v += __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(v), C, R, 0xf, B));
+  MOE_DPP_ADD(0x111, 0xf, true)   // row_shr:1
+  MOE_DPP_ADD(0x112, 0xf, true)   // row_shr:2
+  MOE_DPP_ADD(0x114, 0xf, true)   // row_shr:4
+  MOE_DPP_ADD(0x118, 0xf, true)   // row_shr:8
+  MOE_DPP_ADD(0x142, 0xa, false)  // row_bcast:15 -> rows 1, 3
+  MOE_DPP_ADD(0x143, 0xc, false)  // row_bcast:31 -> rows 2, 3
+#undef MOE_DPP_ADD
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), kWave - 1));
+}
+
 // In-place exclusive scan of a[0..n) in LDS by wave 0 of the block (n <= 64*16).
 // Writes the total to a[n]. Caller synchronises before and after.
 __device__ __forceinline__ void wave0_exclusive_scan(int *a, int n) {

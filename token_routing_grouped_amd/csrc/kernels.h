@@ -18,6 +18,10 @@ struct MetaOut {
       *s_reverse_scatter_idx, *tok_off;
   float *router_scores;
   uint32_t *status;
+  // router only: aux = aux_scale * sum_e count_e * psum[e] (written by workgroup 0)
+  float *aux = nullptr;
+  const float *psum = nullptr;
+  float aux_scale = 0.0f;
 };
 
 inline int meta_blocks(int64_t NK) {
@@ -45,10 +49,19 @@ inline size_t meta_workspace_bytes(int64_t NK, int E) {
 }
 hipError_t launch_meta_hist(const int32_t *topk_idx, int N, int K, int E, int32_t *ws,
                             hipStream_t stream);
-hipError_t launch_meta_scan(int N, int K, int E, int32_t *ws, hipStream_t stream);
+// fcol (router only, else null): E float columns [E][nblk] whose fixed-order sums go
+// to fsum [E]
+hipError_t launch_meta_scan(int N, int K, int E, int32_t *ws, hipStream_t stream,
+                            const float *fcol = nullptr, float *fsum = nullptr);
 hipError_t launch_meta_scatter(const int32_t *topk_idx, const float *topk_weights, int N, int K,
                                int E, int capacity, const int32_t *ws, const MetaOut &out,
                                hipStream_t stream);
+
+// ---- router (top-K + the metadata histogram pass, and the aux loss) ---------
+size_t route_ws_floats(int64_t NK, int E);  // per-chunk P sums [E][nblk], then their totals [E]
+hipError_t launch_route_hist(const void *logits, bool bf16, int N, int E, int K, int mode,
+                             int renorm, bool want_p, int32_t *topk_idx, float *topk_w,
+                             int32_t *meta_ws, float *ppart, hipStream_t stream);
 
 // ---- grouped GEMMs (bf16 MFMA) ----------------------------------------------
 // Two schedules:

@@ -62,12 +62,29 @@ __global__ __launch_bounds__(kMetaThreads) void meta_hist_kernel(const int32_t *
 __global__ __launch_bounds__(kMetaThreads) void meta_scan_kernel(const int32_t *__restrict__ hist,
                                                                  int W, int nblk,
                                                                  int32_t *__restrict__ pre,
-                                                                 int32_t *__restrict__ tot) {
+                                                                 int32_t *__restrict__ tot,
+                                                                 const float *__restrict__ fcol,
+                                                                 float *__restrict__ fsum) {
   __shared__ int32_t s_wave[kMetaThreads / kWave];
   const int c = blockIdx.x;
   const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
   const int R = (nblk + kMetaThreads - 1) / kMetaThreads;
   const int b0 = tid * R;
+  if (c >= W) {  // router P column: fixed-order sum (runs, then waves, then wave order)
+    const float *col = fcol + (int64_t)(c - W) * nblk;
+    float s = 0.0f;
+    for (int r = 0; r < R && b0 + r < nblk; r++) s += col[b0 + r];
+    s = wave_sum_dpp_f32(s);
+    float *s_f = (float *)s_wave;
+    if (lane == 0) s_f[w] = s;
+    __syncthreads();
+    if (tid == 0) {
+      float t = 0.0f;
+      for (int i = 0; i < kMetaThreads / kWave; i++) t += s_f[i];
+      fsum[c - W] = t;
+    }
+    return;
+  }
   const int32_t *col = hist + (int64_t)c * nblk;
   constexpr int kReg = 8;
   int v[kReg];
@@ -134,16 +151,25 @@ __global__ __launch_bounds__(kMetaThreads) void meta_scatter_kernel(
     r_w[it] = j < NK ? wts[j] : 0.0f;
   }
   const int32_t *prow = pre + (int64_t)me * W;
+  const bool aux = me == 0 && out.aux;  // router: the load-balancing loss
+  float *s_prod = (float *)(s_misc + 8);  // [E] (router only)
   for (int c = tid; c < W; c += kMetaThreads) {
     s_base[c] = prow[c];
     if (c <= E) {
       const int t = tot[c];
       s_off[c < E ? c : E + 1] = t;
       if (me == 0 && c < E) out.expert_frequency[c] = t;
+      if (aux && c < E) s_prod[c] = out.psum ? (float)t * out.psum[c] : 0.0f;
     }
   }
   for (int i = tid; i < 4 * E + 8; i += kMetaThreads) s_run[i] = 0;
   __syncthreads();
+  if (aux && tid < kWave) {  // lane-strided partials, then the wave sum: fixed order
+    float a = 0.0f;
+    for (int e = tid; e < E; e += kWave) a += s_prod[e];
+    a = wave_sum_dpp_f32(a);
+    if (tid == 0) *out.aux = a * out.aux_scale;
+  }
   wave0_exclusive_scan(s_off, E);  // s_off[e] = expert_frequency_offset[e], [E] = P
   __syncthreads();
   const int P = s_off[E];
@@ -222,10 +248,11 @@ hipError_t launch_meta_hist(const int32_t *topk_idx, int N, int K, int E, int32_
   return hipGetLastError();
 }
 
-hipError_t launch_meta_scan(int N, int K, int E, int32_t *ws, hipStream_t stream) {
+hipError_t launch_meta_scan(int N, int K, int E, int32_t *ws, hipStream_t stream,
+                            const float *fcol, float *fsum) {
   const MetaWs L = meta_ws_layout((int64_t)N * K, E);
-  hipLaunchKernelGGL(meta_scan_kernel, dim3(E + 2), dim3(kMetaThreads), 0, stream, ws + L.hist,
-                     E + 2, L.nblk, ws + L.pre, ws + L.tot);
+  hipLaunchKernelGGL(meta_scan_kernel, dim3(E + 2 + (fcol ? E : 0)), dim3(kMetaThreads), 0, stream,
+                     ws + L.hist, E + 2, L.nblk, ws + L.pre, ws + L.tot, fcol, fsum);
   return hipGetLastError();
 }
 
@@ -235,7 +262,7 @@ hipError_t launch_meta_scatter(const int32_t *topk_idx, const float *topk_weight
   const MetaWs L = meta_ws_layout((int64_t)N * K, E);
   int nbits = 0;
   while ((1 << nbits) < E) nbits++;
-  const size_t sh = (size_t)(2 * (E + 2) + 4 * E + 8) * sizeof(int32_t);
+  const size_t sh = (size_t)(2 * (E + 2) + 4 * E + 8 + (out.aux ? E : 0)) * sizeof(int32_t);
   hipLaunchKernelGGL(meta_scatter_kernel, dim3(L.nblk), dim3(kMetaThreads), sh, stream, topk_idx,
                      topk_weights, N, K, E, nbits, capacity, ws + L.pre, ws + L.tot, out);
   return hipGetLastError();
