@@ -115,7 +115,7 @@ __global__ __launch_bounds__(CT) void combine_kernel(const T *__restrict__ y,
 #pragma unroll
     for (int i = 0; i < CHUNKS; i++) {
       const int c = c0 + i * 64 + lane;
-      if (c < nchunk) orow[c] = Vec<T>::pack(acc[i]);
+      if (c < nchunk) __builtin_nontemporal_store(Vec<T>::pack(acc[i]), orow + c);  // final output
     }
   }
 

@@ -407,7 +407,10 @@ void gemm_bf16_kernel(GemmArgs g) {
       } else {
         off = (int64_t)e * g.c_es + (int64_t)(mt * BM + row) * g.ldc;
       }
-      *(u32x4 *)(C + off + (int64_t)nt * BN + ch * 8) = *(const u32x4 *)(Cs + row * CLD + ch * 8);
+      // streaming store: a whole-chip burst of output tiles would otherwise fill L2
+      // with dirty lines ahead of the operands other tiles still read
+      __builtin_nontemporal_store(*(const u32x4 *)(Cs + row * CLD + ch * 8),
+                                  (u32x4 *)(C + off + (int64_t)nt * BN + ch * 8));
     }
   } else if constexpr (SWI) {
     uint16_t *Hs = (uint16_t *)g.C;  // may be null (inference); always interleaved
