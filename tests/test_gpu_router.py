@@ -108,3 +108,10 @@ def test_route_then_forward():
     m = oracle.build_metadata(ref["topk_idx"], ref["topk_weights"].astype(np.float32), E)
     f = oracle.forward(f64(d["x"]), f64(d["w_up"]), f64(d["w_down"]), m)
     assert_close(np64(out), f["out"], TOL["bf16"], "out")
+
+
+def test_route_long_columns():
+    """Over 2048 metadata chunks: the counts and the aux loss's probability columns are
+    reduced in two passes."""
+    lg = synth.router_logits(150000, 64, seed=21)
+    check(*run_route(lg, 8, 1, False))

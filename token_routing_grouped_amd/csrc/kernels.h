@@ -29,19 +29,24 @@ inline int meta_blocks(int64_t NK) {
   return b < 1 ? 1 : (int)b;
 }
 // metadata workspace, in int32 elements: per-chunk histogram columns [E+2][nblk],
-// per-chunk exclusive prefixes [nblk][E+2], column totals [E+2]
+// per-chunk exclusive prefixes [nblk][E+2], column totals [E+2], and the segment sums
+// of the two-pass scan for long columns ([2E+2][nseg]: the E+2 count columns, then the
+// router's E probability columns)
+constexpr int kScanSeg = kMetaThreads * 8;  // chunks per scan segment (8 per thread)
 struct MetaWs {
-  int nblk;
-  size_t hist, pre, tot, total;
+  int nblk, nseg;
+  size_t hist, pre, tot, seg, total;
 };
 inline MetaWs meta_ws_layout(int64_t NK, int E) {
   MetaWs L;
   L.nblk = meta_blocks(NK);
+  L.nseg = (L.nblk + kScanSeg - 1) / kScanSeg;
   const size_t cells = (size_t)L.nblk * (size_t)(E + 2);
   L.hist = 0;
   L.pre = cells;
   L.tot = 2 * cells;
-  L.total = 2 * cells + (size_t)(E + 2);
+  L.seg = L.tot + (size_t)(E + 2);
+  L.total = L.seg + (size_t)(2 * E + 2) * (size_t)L.nseg;
   return L;
 }
 inline size_t meta_workspace_bytes(int64_t NK, int E) {

@@ -11,9 +11,10 @@
 //  1. meta_hist: each workgroup counts its chunk per expert (LDS integer atomics),
 //     flags ids outside [-1,E) and counts its valid slots. Columns: E experts,
 //     the flag, the valid count; stored column-major [E+2][nblk].
-//  2. meta_scan: one workgroup per column: exclusive prefix over chunks (each
-//     thread sums a run of consecutive chunks, then DPP scans inside wavefronts),
-//     stored row-major [nblk][E+2], and the column total.
+//  2. meta_scan: one workgroup per column segment of up to 2048 chunks: exclusive
+//     prefix over chunks (each thread sums 8 consecutive chunks, then DPP scans
+//     inside wavefronts), stored row-major [nblk][E+2], and the column total; long
+//     columns take a first pass of segment sums.
 //  3. meta_scatter: each workgroup reads its row of prefixes and the totals (one
 //     memory round trip), scans the totals into expert_frequency_offset, then
 //     ranks its own slots stably: inside a wavefront the lanes holding the same
@@ -56,70 +57,94 @@ __global__ __launch_bounds__(kMetaThreads) void meta_hist_kernel(const int32_t *
     hist[(int64_t)e * gridDim.x + blockIdx.x] = sh[e];
 }
 
-// One workgroup per column c of hist: pre[b][c] = sum of hist[c][b'] over b' < b,
-// tot[c] = the column's sum. Thread i covers chunks [i*R, i*R+R); the thread sums
+// Column scans. Column c of hist (c < W) gives pre[b][c] = sum of hist[c][b'] over
+// b' < b and tot[c] = the column's sum; the router's probability columns (c >= W,
+// fcol) only need their sums. A column is cut into segments of kScanSeg chunks, one
+// workgroup each; thread i of a segment covers 8 consecutive chunks, the thread sums
 // are scanned with DPP inside each wavefront and the four wavefront totals in LDS.
-__global__ __launch_bounds__(kMetaThreads) void meta_scan_kernel(const int32_t *__restrict__ hist,
-                                                                 int W, int nblk,
-                                                                 int32_t *__restrict__ pre,
-                                                                 int32_t *__restrict__ tot,
-                                                                 const float *__restrict__ fcol,
-                                                                 float *__restrict__ fsum) {
-  __shared__ int32_t s_wave[kMetaThreads / kWave];
-  const int c = blockIdx.x;
+// Columns of more than one segment take two passes: pass 0 writes each segment's
+// sum, pass 1 adds the sums of the earlier segments (in order) as the base.
+template <typename T>
+__device__ __forceinline__ T segment_sum_scan(const T *__restrict__ col, int c0, int n, T *v,
+                                              T *run_out, T *s_wave) {
   const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
-  const int R = (nblk + kMetaThreads - 1) / kMetaThreads;
-  const int b0 = tid * R;
-  if (c >= W) {  // router P column: fixed-order sum (runs, then waves, then wave order)
-    const float *col = fcol + (int64_t)(c - W) * nblk;
-    float s = 0.0f;
-    for (int r = 0; r < R && b0 + r < nblk; r++) s += col[b0 + r];
-    s = wave_sum_dpp_f32(s);
-    float *s_f = (float *)s_wave;
-    if (lane == 0) s_f[w] = s;
-    __syncthreads();
+  const int b0 = c0 + tid * 8;
+  T s = 0;
+#pragma unroll
+  for (int r = 0; r < 8; r++) {
+    v[r] = (tid * 8 + r < n) ? col[b0 + r] : (T)0;
+    s += v[r];
+  }
+  T incl;
+  if constexpr (std::is_integral<T>::value) {
+    incl = wave_inclusive_scan_dpp(s);
+  } else {
+    incl = wave_sum_dpp_f32(s);  // floats: only the total is used
+  }
+  if (lane == kWave - 1) s_wave[w] = incl;
+  __syncthreads();
+  T run = incl - s, total = 0;
+#pragma unroll
+  for (int i = 0; i < kMetaThreads / kWave; i++) {
+    const T t = s_wave[i];
+    run += i < w ? t : (T)0;
+    total += t;
+  }
+  *run_out = run;
+  return total;
+}
+
+__global__ __launch_bounds__(kMetaThreads) void meta_scan_kernel(
+    const int32_t *__restrict__ hist, int W, int nblk, int nseg, int pass,
+    int32_t *__restrict__ pre, int32_t *__restrict__ tot, int32_t *__restrict__ segsum,
+    const float *__restrict__ fcol, float *__restrict__ fsum, float *__restrict__ fsegsum,
+    int Wf) {
+  __shared__ int32_t s_wave[kMetaThreads / kWave];
+  __shared__ int32_t s_base;
+  const int ncol = W + Wf;
+  const int c = blockIdx.x % ncol, seg = blockIdx.x / ncol;
+  const int tid = threadIdx.x;
+  const int c0 = seg * kScanSeg;
+  const int n = min(kScanSeg, nblk - c0);  // chunks in this segment
+  if (c >= W) {  // router probability column: fixed-order sums
+    const int cf = c - W;
+    if (pass == 1 && nseg > 1) {
+      if (seg == 0 && tid == 0) {
+        float t = 0.0f;
+        for (int q = 0; q < nseg; q++) t += fsegsum[(int64_t)cf * nseg + q];
+        fsum[cf] = t;
+      }
+      return;
+    }
+    float v[8], run;
+    const float t = segment_sum_scan<float>(fcol + (int64_t)cf * nblk, c0, n, v, &run,
+                                            (float *)s_wave);
     if (tid == 0) {
-      float t = 0.0f;
-      for (int i = 0; i < kMetaThreads / kWave; i++) t += s_f[i];
-      fsum[c - W] = t;
+      if (nseg > 1) fsegsum[(int64_t)cf * nseg + seg] = t;
+      else fsum[cf] = t;
     }
     return;
   }
+  int v[8], run;
   const int32_t *col = hist + (int64_t)c * nblk;
-  constexpr int kReg = 8;
-  int v[kReg];
-  int s = 0;
-  if (R <= kReg) {
-#pragma unroll
-    for (int r = 0; r < kReg; r++) v[r] = (r < R && b0 + r < nblk) ? col[b0 + r] : 0;
-#pragma unroll
-    for (int r = 0; r < kReg; r++) s += v[r];
-  } else {
-    for (int r = 0; r < R && b0 + r < nblk; r++) s += col[b0 + r];
+  const int t = segment_sum_scan<int32_t>(col, c0, n, v, &run, s_wave);
+  if (pass == 0) {  // segment sums of a long column
+    if (tid == 0) segsum[(int64_t)c * nseg + seg] = t;
+    return;
   }
-  const int incl = wave_inclusive_scan_dpp(s);
-  if (lane == kWave - 1) s_wave[w] = incl;
+  if (tid == 0) {
+    int base = 0;
+    for (int q = 0; q < seg; q++) base += segsum[(int64_t)c * nseg + q];
+    s_base = base;
+  }
   __syncthreads();
-  int run = incl - s, total = 0;
+  run += s_base;
 #pragma unroll
-  for (int i = 0; i < kMetaThreads / kWave; i++) {
-    const int t = s_wave[i];
-    run += i < w ? t : 0;
-    total += t;
+  for (int r = 0; r < 8; r++) {
+    if (tid * 8 + r < n) pre[(int64_t)(c0 + tid * 8 + r) * W + c] = run;
+    run += v[r];
   }
-  if (R <= kReg) {
-#pragma unroll
-    for (int r = 0; r < kReg; r++) {
-      if (r < R && b0 + r < nblk) pre[(int64_t)(b0 + r) * W + c] = run;
-      run += v[r];
-    }
-  } else {  // long runs: a second pass over the (cached) run
-    for (int r = 0; r < R && b0 + r < nblk; r++) {
-      pre[(int64_t)(b0 + r) * W + c] = run;
-      run += col[b0 + r];
-    }
-  }
-  if (tid == 0) tot[c] = total;
+  if (tid == 0 && seg == nseg - 1) tot[c] = s_base + t;
 }
 
 __global__ __launch_bounds__(kMetaThreads) void meta_scatter_kernel(
@@ -136,7 +161,15 @@ __global__ __launch_bounds__(kMetaThreads) void meta_scatter_kernel(
   const int w = tid / kWave;
   const int lane = tid % kWave;
   const int64_t NK = (int64_t)N * K;
-  const int me = blockIdx.x;
+  // chunk of this workgroup: each XCD (workgroup id modulo 8) takes a contiguous run
+  // of chunks, so the sorted-position writes of consecutive chunks into an expert's
+  // segment meet in one L2 and leave it as whole lines
+  int me;
+  {
+    const int b = blockIdx.x, G = gridDim.x, x = b % kNumXcd, i = b / kNumXcd;
+    const int q = G / kNumXcd, r = G % kNumXcd;
+    me = x * q + (x < r ? x : r) + i;
+  }
   const int W = E + 2;
 
   // this wave's slots (the w-th quarter of the chunk, rounds of 64), the chunk's
@@ -251,8 +284,18 @@ hipError_t launch_meta_hist(const int32_t *topk_idx, int N, int K, int E, int32_
 hipError_t launch_meta_scan(int N, int K, int E, int32_t *ws, hipStream_t stream,
                             const float *fcol, float *fsum) {
   const MetaWs L = meta_ws_layout((int64_t)N * K, E);
-  hipLaunchKernelGGL(meta_scan_kernel, dim3(E + 2 + (fcol ? E : 0)), dim3(kMetaThreads), 0, stream,
-                     ws + L.hist, E + 2, L.nblk, ws + L.pre, ws + L.tot, fcol, fsum);
+  const int W = E + 2, Wf = fcol ? E : 0;
+  int32_t *segsum = ws + L.seg;
+  float *fsegsum = (float *)(segsum + (size_t)W * L.nseg);
+  const dim3 grid((unsigned)((W + Wf) * L.nseg));
+  if (L.nseg > 1) {
+    hipLaunchKernelGGL(meta_scan_kernel, grid, dim3(kMetaThreads), 0, stream, ws + L.hist, W,
+                       L.nblk, L.nseg, 0, ws + L.pre, ws + L.tot, segsum, fcol, fsum, fsegsum, Wf);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(meta_scan_kernel, grid, dim3(kMetaThreads), 0, stream, ws + L.hist, W,
+                     L.nblk, L.nseg, 1, ws + L.pre, ws + L.tot, segsum, fcol, fsum, fsegsum, Wf);
   return hipGetLastError();
 }
 
