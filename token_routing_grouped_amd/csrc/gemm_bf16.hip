@@ -527,6 +527,9 @@ hipError_t launch_tiles(int bm, int bn, int bk, int grid, const GemmArgs &g, hip
                        dim3(grid), dim3(64 * WGM_ * WGN_), 0, st, g);                    \
     return hipGetLastError();                                                             \
   }
+  if constexpr (MODE == GROUPED_M) {
+    MOE_LAUNCH(32, 128, 64, 1, 2)
+  }
   MOE_LAUNCH(128, 128, 64, 2, 2)
   MOE_LAUNCH(128, 128, 32, 2, 2)
   MOE_LAUNCH(256, 256, 64, 2, 4)
@@ -542,7 +545,8 @@ hipError_t launch_tiles(int bm, int bn, int bk, int grid, const GemmArgs &g, hip
 }  // namespace
 
 // Tile shape per GEMM: 256x256x32 with eight waves where the fixed dimensions allow it
-// (half the bytes per flop of 128x128), else 128x128.
+// (half the bytes per flop of 128x128), else 128x128; 32x128x64 with two waves when the
+// capacity averages at most 16 rows per expert.
 #ifndef MOE_GM_BIG
 #define MOE_GM_BIG 1
 #endif
@@ -563,10 +567,13 @@ void gemm_tile(GemmKind kind, const GemmArgs &g, int *bm, int *bn, int *bk) {
     *bn = big ? 256 : 128;
     *bk = big ? 32 : MOE_TILE_VK_BK;
   } else {
+    // few rows per expert (decode): 32-row tiles, so the matrix work per streamed
+    // weight byte matches the rows there are and many more workgroups stream weights
+    const bool skinny = (int64_t)g.cap <= 16LL * g.E && g.N % 128 == 0 && g.K % 64 == 0;
     const bool big = MOE_GM_BIG && g.N % 256 == 0 && g.K % 32 == 0;
-    *bm = big ? 256 : 128;
-    *bn = big ? 256 : 128;
-    *bk = big ? 32 : (g.K % MOE_TILE_GM_BK == 0 ? MOE_TILE_GM_BK : 32);
+    *bm = skinny ? 32 : big ? 256 : 128;
+    *bn = skinny ? 128 : big ? 256 : 128;
+    *bk = skinny ? 64 : big ? 32 : (g.K % MOE_TILE_GM_BK == 0 ? MOE_TILE_GM_BK : 32);
   }
 }
 
