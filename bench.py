@@ -33,6 +33,21 @@ PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 # algorithmic flops of each GEMM kernel per launch, in units of P*H*I
 GEMM_FLOPS = {"up_swiglu": 4, "down": 2, "down_bwd": 2, "wgrad_down": 2, "up_bwd": 4,
               "wgrad_up": 4}
+RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)  # flop/byte where the rooflines meet
+
+
+def gemm_bytes(kernel, N, H, I, P, active):
+    """Algorithmic HBM bytes of one launch (bf16): each operand and result once; the
+    weights of the experts that have rows (`active` of them)."""
+    w_up, w_down = active * H * 2 * I * 2, active * I * H * 2
+    return {
+        "up_swiglu": 2 * P * H + w_up + 2 * P * 2 * I + 2 * P * I,   # x rows, W_up, h, a
+        "down": 2 * P * I + w_down + 2 * P * H,                      # a, W_down, y
+        "down_bwd": 2 * P * H + w_down + 2 * P * 2 * I * 2 + 2 * P * I,  # dout rows, W_down, h, dh, w*a
+        "wgrad_down": 2 * P * I + 2 * P * H + w_down,                # w*a, dout rows, dW_down
+        "up_bwd": 2 * P * 2 * I + w_up + 2 * P * H,                  # dh, W_up, dxg
+        "wgrad_up": 2 * P * H + 2 * P * 2 * I + w_up,                # x rows, dh, dW_up
+    }[kernel]
 
 
 def source_digest() -> str:
@@ -357,7 +372,22 @@ def main():
     tflops = flops_step / (ms * 1e-3) / 1e12
     dom_flops = GEMM_FLOPS[dominant] * P * H * I
     dom_tflops = dom_flops / (dom_ms * 1e-3) / 1e12
+    active = int((np.bincount(d["topk_idx"][d["topk_idx"] >= 0].ravel(), minlength=E) > 0).sum())
+    dom_bytes = gemm_bytes(dominant, N, H, I, P, active)
+    # the roofline that bounds the kernel: HBM below the ridge intensity (decode), else MFMA
+    hbm_bound = dom_flops / dom_bytes < RIDGE
     traffic = counted_traffic(dominant, args.workload)
+    if hbm_bound:
+        roof = {"kernel": dominant, "bound": "hbm",
+                "achieved": round(dom_bytes / (dom_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": round(dom_bytes / (dom_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+    else:
+        roof = {"kernel": dominant, "bound": "mfma", "achieved": round(dom_tflops, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4)}
+    roof.update({"traffic": traffic, "avg_us": round(dom_ms * 1e3, 2),
+                 "flops_per_launch": dom_flops, "bytes_per_launch": dom_bytes,
+                 "intensity_flop_per_byte": round(dom_flops / dom_bytes, 1)})
 
     res = {
         "metric": METRIC,
@@ -385,11 +415,7 @@ def main():
                      "GBps": round(meta_bytes / (meta_us * 1e-6) / 1e9, 1),
                      "hbm_frac": round(meta_bytes / (meta_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)},
         "kernels_us": {k: round(v, 1) for k, v in kernel_us.items()},
-        "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(dom_tflops, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "avg_us": round(dom_ms * 1e3, 2),
-                     "flops_per_launch": dom_flops},
+        "roofline": roof,
         "wall_s_timed": round(wall, 4),
     }
     res["router"] = router_timing(moe, synth, torch, np)
