@@ -107,6 +107,8 @@ void gemm_bf16_kernel(GemmArgs g) {
   constexpr int A_LD = BM * BK / (8 * NT);  // 16-byte chunks per thread per stage
   constexpr int B_LD = BN * BK / (8 * NT);
   __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM];
+  // EPI_DSWIGLU: router weight of every tile row, fetched while the main loop starts
+  __shared__ __attribute__((aligned(16))) float s_wq[EPI == EPI_DSWIGLU ? BM : 4];
   int *s_pref = (int *)smem;  // expert tile table, used before the first stage is written
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -351,6 +353,10 @@ void gemm_bf16_kernel(GemmArgs g) {
     MOE_LOAD(ra1, rb1, ia1, ib1, kof(1));
     MOE_STORE(ra0, rb0, 0);
     MOE_LOAD(ra0, rb0, ia0, ib0, kof(2));
+    if constexpr (EPI == EPI_DSWIGLU) {
+      for (int r = tid; r < BM; r += NT)
+        s_wq[r] = r < rows ? g.scores[g.s_scatter[row0 + r]] : 0.0f;
+    }
     __syncthreads();
     int kt = 0;
     // steady state, free of branches: the wait before a stage store only holds back
@@ -488,63 +494,57 @@ void gemm_bf16_kernel(GemmArgs g) {
     uint16_t *__restrict__ dH = (uint16_t *)g.C;
     uint16_t *__restrict__ AW = (uint16_t *)g.C2;
     const uint16_t *__restrict__ Hs = (const uint16_t *)g.Hs;
-    const float *__restrict__ scores = g.scores;
-    const int32_t *__restrict__ s_scatter = g.s_scatter;
     float *red = (float *)smem;  // [WGN][BM] row partials of the column waves (the
                                  // loop's final barrier has released the stages)
+    // The saved (gate, up) pairs of the next (mi, ni) block are loaded while the current
+    // block is computed: each register is refilled right after its value is consumed, so
+    // one block of loads is always in flight. Rows past the segment read row 0 of the
+    // tile and are never stored.
+    uint32_t hv[16];
+    auto h_addr = [&](int mi_, int ni_, int r) {
+      const int j_ = nt * BN + wn * WN + ni_ * 32 + col_l;
+      const int row_ = wm * WM + mi_ * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+      const int64_t s_ = row0 + (row_ < rows ? row_ : 0);
+      return (const uint32_t *)(Hs + s_ * g.ldh + 2 * j_);
+    };
+#pragma unroll
+    for (int r = 0; r < 16; r++) hv[r] = *h_addr(0, 0, r);
 #pragma unroll
     for (int mi = 0; mi < TM; mi++) {
-      // all loads of this row block first: router weights and saved (gate, up) pairs;
-      // rows past the segment read row 0 of the tile and are never stored
-      int64_t srow[16];
-      float wq[16];
-      uint32_t hv[TN][16];
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int row = wm * WM + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        srow[r] = row0 + (row < rows ? row : 0);
-      }
-      int qv[16];
-#pragma unroll
-      for (int r = 0; r < 16; r++) qv[r] = s_scatter[srow[r]];
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        wq[r] = scores[qv[r]];
-#pragma unroll
-        for (int ni = 0; ni < TN; ni++) {
-          const int j = nt * BN + wn * WN + ni * 32 + col_l;
-          hv[ni][r] = *(const uint32_t *)(Hs + srow[r] * g.ldh + 2 * j);
-        }
-      }
       float part[16];
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int row = wm * WM + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        const bool ok = row < rows;
-        part[r] = 0.0f;
+      for (int r = 0; r < 16; r++) part[r] = 0.0f;
 #pragma unroll
-        for (int ni = 0; ni < TN; ni++) {
-          const int j = nt * BN + wn * WN + ni * 32 + col_l;
-          const float gt = bf16_to_f32((uint16_t)(hv[ni][r] & 0xffffu));
-          const float up = bf16_to_f32((uint16_t)(hv[ni][r] >> 16));
+      for (int ni = 0; ni < TN; ni++) {
+        constexpr int NB = TM * TN;
+        const int b = mi * TN + ni;
+        const int j = nt * BN + wn * WN + ni * 32 + col_l;
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const int row = wm * WM + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const int64_t srow = row0 + row;
+          const float wq = s_wq[row];
+          const uint32_t h2 = hv[r];
+          if (b + 1 < NB) hv[r] = *h_addr((b + 1) / TN, (b + 1) % TN, r);
+          const float gt = bf16_to_f32((uint16_t)(h2 & 0xffffu));
+          const float up = bf16_to_f32((uint16_t)(h2 >> 16));
           const float dau = acc[mi][ni][r];
           const float sg = sigmoid_f(gt);
           const float a = gt * sg * up;
-          part[r] += dau * a;
-          const float da = wq[r] * dau;
-          const float dg = da * up * sg * (1.0f + gt * (1.0f - sg));
-          const float du = da * gt * sg;
-          if (ok) {
+          if (row < rows) {
+            part[r] += dau * a;
+            const float da = wq * dau;
+            const float dg = da * up * sg * (1.0f + gt * (1.0f - sg));
+            const float du = da * gt * sg;
             if (g.gu_concat) {  // dh in W_up's column order
-              dH[srow[r] * g.ldc + j] = f32_to_bf16(dg);
-              dH[srow[r] * g.ldc + g.N + j] = f32_to_bf16(du);
+              dH[srow * g.ldc + j] = f32_to_bf16(dg);
+              dH[srow * g.ldc + g.N + j] = f32_to_bf16(du);
             } else {
-              *(uint32_t *)(dH + srow[r] * g.ldc + 2 * j) = pack_bf16x2(dg, du);
+              *(uint32_t *)(dH + srow * g.ldc + 2 * j) = pack_bf16x2(dg, du);
             }
-            AW[srow[r] * g.ldc2 + j] = f32_to_bf16(wq[r] * a);
+            AW[srow * g.ldc2 + j] = f32_to_bf16(wq * a);
           }
         }
-        if (!ok) part[r] = 0.0f;
       }
       // butterfly over the 32 lanes of each half: after exchanging half of the
       // values at each step, lane l holds the full row sum for r = (l%32)/2
