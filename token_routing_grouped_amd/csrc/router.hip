@@ -12,9 +12,10 @@
 // gives no formula).
 //
 // route_hist: 16 lanes per token (E <= 256, K <= 16; four tokens per wavefront), else
-// a whole wavefront per token. The K experts come from K rounds of a group maximum
-// over 64-bit keys (order-preserving logit bits, then the inverted expert id) taken
-// with DPP lane moves, so the choice is exact and deterministic. Each workgroup owns one chunk of kMetaChunk slots of the flattened
+// a whole wavefront per token; each lane holds NV (a power of two, from E) logits. The
+// K experts come from K rounds of two group reductions taken with DPP lane moves: the
+// maximum of the order-preserving logit bits, then the lowest expert id holding it, so
+// the choice is exact and deterministic. Each workgroup owns one chunk of kMetaChunk slots of the flattened
 // [N,K] layout, exactly like the metadata histogram pass: it writes the slots of its
 // chunk (tokens straddling a chunk edge are evaluated by both workgroups, each writing
 // its own slots), counts them per expert into its histogram column, and sums the full
@@ -29,7 +30,10 @@ namespace moe {
 namespace {
 
 constexpr int kMaxPerLane = 16;  // experts per lane: E <= 16 * lanes per token
-constexpr int kRouteThreads = 1024;  // 16 wavefronts share one chunk of kMetaChunk slots
+#ifndef MOE_ROUTE_THREADS
+#define MOE_ROUTE_THREADS 512
+#endif
+constexpr int kRouteThreads = MOE_ROUTE_THREADS;  // wavefronts sharing one chunk of slots
 
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(uint16_t v) { return bf16_to_f32(v); }
@@ -53,38 +57,6 @@ template <int CTRL, int ROWS, bool BC>
 __device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROWS, 0xf, BC);
 }
-__device__ __forceinline__ uint64_t max64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
-template <int LPT>
-__device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
-  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-#define MOE_STEP(C, R, B)                                                       \
-  {                                                                             \
-    const uint32_t l2 = dpp<C, R, B>(0u, lo), h2 = dpp<C, R, B>(0u, hi);        \
-    const uint64_t m = max64(((uint64_t)hi << 32) | lo, ((uint64_t)h2 << 32) | l2); \
-    lo = (uint32_t)m;                                                           \
-    hi = (uint32_t)(m >> 32);                                                   \
-  }
-  if constexpr (LPT == 16) {
-    MOE_STEP(0x121, 0xf, false)  // row_ror:1
-    MOE_STEP(0x122, 0xf, false)  // row_ror:2
-    MOE_STEP(0x124, 0xf, false)  // row_ror:4
-    MOE_STEP(0x128, 0xf, false)  // row_ror:8
-    return ((uint64_t)hi << 32) | lo;
-  } else {
-    MOE_STEP(0x111, 0xf, true)   // row_shr:1
-    MOE_STEP(0x112, 0xf, true)   // row_shr:2
-    MOE_STEP(0x114, 0xf, true)   // row_shr:4
-    MOE_STEP(0x118, 0xf, true)   // row_shr:8
-    MOE_STEP(0x142, 0xa, false)  // row_bcast:15 -> rows 1, 3
-    MOE_STEP(0x143, 0xc, false)  // row_bcast:31 -> rows 2, 3
-    const uint32_t l = __builtin_amdgcn_readlane(lo, kWave - 1);
-    const uint32_t h = __builtin_amdgcn_readlane(hi, kWave - 1);
-    return ((uint64_t)h << 32) | l;
-  }
-#undef MOE_STEP
-}
-
 template <int LPT>
 __device__ __forceinline__ float group_max_f32(float v) {
   const uint32_t NEG_INF = 0xff800000u;
@@ -103,6 +75,34 @@ __device__ __forceinline__ float group_max_f32(float v) {
     MOE_STEP(0x142, 0xa, false)
     MOE_STEP(0x143, 0xc, false)
     return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), kWave - 1));  // bits
+  }
+#undef MOE_STEP
+}
+
+// unsigned max / min over the token's lanes (ID: the identity, fed to lanes a shift
+// leaves without a source)
+template <int LPT, bool MAX>
+__device__ __forceinline__ uint32_t group_ext_u32(uint32_t v) {
+  constexpr uint32_t ID = MAX ? 0u : 0xffffffffu;
+#define MOE_STEP(C, R, B)                                                       \
+  {                                                                             \
+    const uint32_t o_ = dpp<C, R, B>(ID, v);                                    \
+    v = MAX ? (o_ > v ? o_ : v) : (o_ < v ? o_ : v);                            \
+  }
+  if constexpr (LPT == 16) {
+    MOE_STEP(0x121, 0xf, false)
+    MOE_STEP(0x122, 0xf, false)
+    MOE_STEP(0x124, 0xf, false)
+    MOE_STEP(0x128, 0xf, false)
+    return v;
+  } else {
+    MOE_STEP(0x111, 0xf, false)
+    MOE_STEP(0x112, 0xf, false)
+    MOE_STEP(0x114, 0xf, false)
+    MOE_STEP(0x118, 0xf, false)
+    MOE_STEP(0x142, 0xa, false)
+    MOE_STEP(0x143, 0xc, false)
+    return __builtin_amdgcn_readlane(v, kWave - 1);
   }
 #undef MOE_STEP
 }
@@ -131,10 +131,10 @@ __device__ __forceinline__ float group_sum_f32(float v) {
 // sum over the whole wave, the same value in every lane
 __device__ __forceinline__ float wave_sum_f32(float v) { return group_sum_f32<64>(v); }
 
-// LPT lanes per token (16: E <= 256 and K <= 16, four tokens per wave; else 64).
-// Lane s of a token's group holds experts s, s+LPT, ...; after the selection, lane k
-// of the group holds the k-th expert.
-template <typename T, int LPT>
+// LPT lanes per token (16: E <= 256 and K <= 16, four tokens per wave; else 64), NV
+// logits per lane. Lane s of a token's group holds experts s, s+LPT, ...; after the
+// selection, lane k of the group holds the k-th expert.
+template <typename T, int LPT, int NV>
 __global__ __launch_bounds__(kRouteThreads) void route_hist_kernel(
     const T *__restrict__ logits, int N, int E, int K, int mode, int renorm, int want_p,
     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, int32_t *__restrict__ hist,
@@ -149,17 +149,15 @@ __global__ __launch_bounds__(kRouteThreads) void route_hist_kernel(
   const int sub = lane / LPT, sl = lane % LPT;
   const int b = blockIdx.x, nblk = gridDim.x;
   for (int i = tid; i < E + 2; i += kRouteThreads) s_cnt[i] = 0;
-  for (int i = tid; i < NW * E; i += kRouteThreads) s_p[i] = 0.0f;
   __syncthreads();
 
   const int64_t NK = (int64_t)N * K;
   const int64_t j0 = (int64_t)b * kMetaChunk;
   const int64_t j1 = min(j0 + kMetaChunk, NK);  // this workgroup's slots [j0, j1)
   const int t0 = (int)(j0 / K), t1 = j1 > j0 ? (int)((j1 - 1) / K) : t0 - 1;
-  const int nv = (E + LPT - 1) / LPT;
-  float pacc[kMaxPerLane];
+  float pacc[NV];
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; i++) pacc[i] = 0.0f;
+  for (int i = 0; i < NV; i++) pacc[i] = 0.0f;
   int nslots = 0;
 
   // uniform trip count for the whole wave; lanes of a token past t1 compute on a
@@ -167,46 +165,54 @@ __global__ __launch_bounds__(kRouteThreads) void route_hist_kernel(
   for (int base = t0 + w * TPW; base <= t1; base += TPB) {
     const bool live = base + sub <= t1;
     const int t = live ? base + sub : t1;
-    float v[kMaxPerLane];
+    float v[NV];
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; i++) {
+    for (int i = 0; i < NV; i++) {
       const int e = sl + LPT * i;
-      v[i] = (i < nv && e < E) ? to_f32(logits[(int64_t)t * E + e]) : -INFINITY;
+      v[i] = e < E ? to_f32(logits[(int64_t)t * E + e]) : -INFINITY;
     }
     float lmax = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; i++) lmax = fmaxf(lmax, v[i]);
+    for (int i = 0; i < NV; i++) lmax = fmaxf(lmax, v[i]);
     const float mx = group_max_f32<LPT>(lmax);
-    float ex[kMaxPerLane];
+    float ex[NV];
     float zl = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; i++) {
-      const int e = sl + LPT * i;
-      ex[i] = (i < nv && e < E) ? expf(v[i] - mx) : 0.0f;
+    for (int i = 0; i < NV; i++) {
+      ex[i] = sl + LPT * i < E ? expf(v[i] - mx) : 0.0f;
       zl += ex[i];
     }
     const float z_all = group_sum_f32<LPT>(zl);
 
-    // K rounds of a group maximum over (logit, inverted id) keys
-    uint32_t taken = 0;
+    // K rounds: the group maximum of the order-preserving logit bits, then the lowest
+    // expert id holding that value (equal logits go to the lower id). A key of 0 marks a
+    // taken or absent expert; valid keys are at least 1 (only the all-ones NaN pattern
+    // is moved, from 0 to 1).
+    uint32_t key[NV];
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+      const uint32_t o = ordered(v[i]);
+      key[i] = sl + LPT * i < E ? (o > 1u ? o : 1u) : 0u;
+    }
     int my_e = 0;
     float my_v = 0.0f;
     for (int k = 0; k < K; k++) {
-      uint64_t best = 0;
+      uint32_t m = 0;
 #pragma unroll
-      for (int i = 0; i < kMaxPerLane; i++) {
-        const int e = sl + LPT * i;
-        if (i < nv && e < E && !((taken >> i) & 1u)) {
-          const uint64_t key = ((uint64_t)ordered(v[i]) << 32) | (uint32_t)(0xffffffffu - e);
-          best = key > best ? key : best;
-        }
+      for (int i = 0; i < NV; i++) m = key[i] > m ? key[i] : m;
+      m = group_ext_u32<LPT, true>(m);
+      uint32_t cand = 0xffffffffu;  // this lane's lowest id holding m
+#pragma unroll
+      for (int i = NV - 1; i >= 0; i--) cand = key[i] == m ? (uint32_t)(sl + LPT * i) : cand;
+      const int e = (int)group_ext_u32<LPT, false>(cand);
+      if (sl == (e % LPT)) {
+#pragma unroll
+        for (int i = 0; i < NV; i++)
+          if (i == e / LPT) key[i] = 0;
       }
-      best = group_max_u64<LPT>(best);
-      const int e = (int)(0xffffffffu - (uint32_t)best);
-      if (sl == (e % LPT)) taken |= 1u << (e / LPT);
       if (sl == k) {
         my_e = e;
-        my_v = unordered((uint32_t)(best >> 32));
+        my_v = unordered(m);
       }
     }
     const float ek = sl < K ? expf(my_v - mx) : 0.0f;
@@ -225,22 +231,25 @@ __global__ __launch_bounds__(kRouteThreads) void route_hist_kernel(
       nslots++;
     }
     if (want_p && live && (int64_t)t * K >= j0) {  // this workgroup owns token t
+      const float rz = 1.0f / z_all;
 #pragma unroll
-      for (int i = 0; i < kMaxPerLane; i++) pacc[i] += ex[i] / z_all;
+      for (int i = 0; i < NV; i++) pacc[i] += ex[i] * rz;
     }
   }
   nslots = (int)wave_sum_f32((float)nslots);
   if (lane == 0) atomicAdd(&s_cnt[E + 1], nslots);
   if (want_p) {
-    // the wave's token groups, in group order, into the wave's LDS row (one wave's
-    // LDS operations complete in issue order)
-    for (int q = 0; q < TPW; q++) {
-      if (sub == q) {
+    // the wave's token groups summed over a fixed tree (lanes sl of every group hold
+    // the same experts), then the first group's lanes write the wave's row
 #pragma unroll
-        for (int i = 0; i < kMaxPerLane; i++) {
-          const int e = sl + LPT * i;
-          if (i < nv && e < E) s_p[w * E + e] += pacc[i];
-        }
+    for (int o = LPT; o < kWave; o <<= 1)
+#pragma unroll
+      for (int i = 0; i < NV; i++) pacc[i] += __shfl_xor(pacc[i], o, kWave);
+    if (sub == 0) {
+#pragma unroll
+      for (int i = 0; i < NV; i++) {
+        const int e = sl + LPT * i;
+        if (e < E) s_p[w * E + e] = pacc[i];
       }
     }
   }
@@ -265,15 +274,27 @@ hipError_t launch_route_hist(const void *logits, bool bf16, int N, int E, int K,
   const size_t sh = (size_t)(E + 2) * sizeof(int32_t) +
                     (size_t)(kRouteThreads / kWave) * E * sizeof(float);
   const bool narrow = E <= 16 * kMaxPerLane && K <= 16;  // 16 lanes per token
-#define MOE_ROUTE(T, LPT)                                                                  \
-  hipLaunchKernelGGL((route_hist_kernel<T, LPT>), dim3(L.nblk), dim3(kRouteThreads), sh, stream, \
-                     (const T *)logits, N, E, K, mode, renorm, (int)want_p, topk_idx, topk_w, \
-                     meta_ws + L.hist, ppart)
-  if (bf16) {
-    if (narrow) MOE_ROUTE(uint16_t, 16); else MOE_ROUTE(uint16_t, 64);
-  } else {
-    if (narrow) MOE_ROUTE(float, 16); else MOE_ROUTE(float, 64);
+  const int lpt = narrow ? 16 : kWave;
+  const int need = (E + lpt - 1) / lpt;  // logits per lane, rounded up to a power of two
+  const int nv = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 16;
+#define MOE_ROUTE(T, LPT, NV)                                                              \
+  hipLaunchKernelGGL((route_hist_kernel<T, LPT, NV>), dim3(L.nblk), dim3(kRouteThreads), sh, \
+                     stream, (const T *)logits, N, E, K, mode, renorm, (int)want_p, topk_idx, \
+                     topk_w, meta_ws + L.hist, ppart)
+#define MOE_ROUTE_NV(T, LPT)                                                               \
+  switch (nv) {                                                                            \
+    case 1: MOE_ROUTE(T, LPT, 1); break;                                                   \
+    case 2: MOE_ROUTE(T, LPT, 2); break;                                                   \
+    case 4: MOE_ROUTE(T, LPT, 4); break;                                                   \
+    case 8: MOE_ROUTE(T, LPT, 8); break;                                                   \
+    default: MOE_ROUTE(T, LPT, 16); break;                                                 \
   }
+  if (bf16) {
+    if (narrow) { MOE_ROUTE_NV(uint16_t, 16) } else { MOE_ROUTE_NV(uint16_t, 64) }
+  } else {
+    if (narrow) { MOE_ROUTE_NV(float, 16) } else { MOE_ROUTE_NV(float, 64) }
+  }
+#undef MOE_ROUTE_NV
 #undef MOE_ROUTE
   return hipGetLastError();
 }
