@@ -86,8 +86,10 @@ __device__ __forceinline__ bf16x8 frag_mn(const uint16_t *tile, int kbase, int c
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// WGM x WGN waves per workgroup; NT threads
-template <int MODE, bool A_KC, bool B_KC, int EPI, int BM, int BN, int BK, int WGM, int WGN>
+// WGM x WGN waves per workgroup; NT threads. GA (varlen-K): bit 0 = the A rows are
+// gathered through a_rows, bit 1 = the B rows through b_rows (else rows are positions).
+template <int MODE, bool A_KC, bool B_KC, int EPI, int BM, int BN, int BK, int WGM, int WGN,
+          int GA>
 __global__ __launch_bounds__(64 * WGM * WGN,
                              (BM * BN > 128 * 128) ? (WGM * WGN == 8 ? 2 : 1) : (BK == 32 ? 3 : 2))
 void gemm_bf16_kernel(GemmArgs g) {
@@ -222,14 +224,17 @@ void gemm_bf16_kernel(GemmArgs g) {
   //  ROWS(ia, ib, k0): (varlen-K) memory rows of the tile at reduction offset k0
 #define MOE_ROWS(ia, ib, k0_)                                                              \
   do {                                                                                     \
+    /* unconditional loads at a clamped position (a per-lane condition around them would  \
+       make the compiler wait for every load in flight, data included, at the join);      \
+       rows past the segment are zeroed where the data is used */                         \
     constexpr int CPA = BM / 8, CPB = BN / 8;                                              \
     _Pragma("unroll") for (int i = 0; i < A_LD; i++) {                                     \
-      const int kk = (k0_) + tid / CPA + (NT / CPA) * i;                                   \
-      ia[i] = kk < seglen ? (g.a_rows ? g.a_rows[seg0 + kk] : seg0 + kk) : -1;             \
+      const int kc = seg0 + min((k0_) + tid / CPA + (NT / CPA) * i, seglen - 1);           \
+      ia[i] = (GA & 1) ? g.a_rows[kc] : kc;                                                \
     }                                                                                      \
     _Pragma("unroll") for (int i = 0; i < B_LD; i++) {                                     \
-      const int kk = (k0_) + tid / CPB + (NT / CPB) * i;                                   \
-      ib[i] = kk < seglen ? (g.b_rows ? g.b_rows[seg0 + kk] : seg0 + kk) : -1;             \
+      const int kc = seg0 + min((k0_) + tid / CPB + (NT / CPB) * i, seglen - 1);           \
+      ib[i] = (GA & 2) ? g.b_rows[kc] : kc;                                                \
     }                                                                                      \
   } while (0)
 
@@ -246,26 +251,29 @@ void gemm_bf16_kernel(GemmArgs g) {
           rb[i] = *(const u32x4 *)(b_ptr[i] + (int64_t)k0 * g.ldb);                        \
       }                                                                                    \
     } else {                                                                               \
-      /* rows were looked up one load earlier (ia/ib); -1 = past the segment -> 0 */       \
+      /* rows were looked up two tiles earlier (ia/ib); rows past the segment are zeroed  \
+         when the set is stored (a select here would wait for these loads at once) */     \
       constexpr int CPA = BM / 8, CPB = BN / 8;                                            \
-      _Pragma("unroll") for (int i = 0; i < A_LD; i++) {                                   \
-        const int64_t r_ = ia[i] < 0 ? 0 : ia[i];                                          \
-        const u32x4 v_ = *(const u32x4 *)(A + r_ * g.lda + (int64_t)mt * BM + (tid % CPA) * 8); \
-        ra[i] = ia[i] < 0 ? u32x4{0, 0, 0, 0} : v_;                                        \
-      }                                                                                    \
-      _Pragma("unroll") for (int i = 0; i < B_LD; i++) {                                   \
-        const int64_t r_ = ib[i] < 0 ? 0 : ib[i];                                          \
-        const u32x4 v_ = *(const u32x4 *)(B + r_ * g.ldb + (int64_t)nt * BN + (tid % CPB) * 8); \
-        rb[i] = ib[i] < 0 ? u32x4{0, 0, 0, 0} : v_;                                        \
-      }                                                                                    \
+      _Pragma("unroll") for (int i = 0; i < A_LD; i++)                                     \
+        ra[i] = *(const u32x4 *)(A + (int64_t)ia[i] * g.lda + (int64_t)mt * BM + (tid % CPA) * 8); \
+      _Pragma("unroll") for (int i = 0; i < B_LD; i++)                                     \
+        rb[i] = *(const u32x4 *)(B + (int64_t)ib[i] * g.ldb + (int64_t)nt * BN + (tid % CPB) * 8); \
       MOE_ROWS(ia, ib, k0 + 2 * BK);                                                       \
     }                                                                                      \
   } while (0)
 
-#define MOE_STORE(ra, rb, st)                                                              \
+#define MOE_STORE(ra, rb, st, tile_)                                                       \
   do {                                                                                     \
     uint16_t *As_ = smem + (st) * STAGE;                                                   \
     uint16_t *Bs_ = As_ + AS::elems;                                                       \
+    if constexpr (MODE == VARLEN_K) { /* rows past the segment -> 0 */                     \
+      constexpr int CPA = BM / 8, CPB = BN / 8;                                            \
+      const int kt_ = (tile_) * BK;                                                        \
+      _Pragma("unroll") for (int i = 0; i < A_LD; i++)                                     \
+        if (kt_ + tid / CPA + (NT / CPA) * i >= seglen) ra[i] = u32x4{0, 0, 0, 0};         \
+      _Pragma("unroll") for (int i = 0; i < B_LD; i++)                                     \
+        if (kt_ + tid / CPB + (NT / CPB) * i >= seglen) rb[i] = u32x4{0, 0, 0, 0};         \
+    }                                                                                      \
     _Pragma("unroll") for (int i = 0; i < A_LD; i++) {                                     \
       if constexpr (A_KC) {                                                                \
         const int r_ = tid / CPK + (NT / CPK) * i;                                         \
@@ -351,7 +359,7 @@ void gemm_bf16_kernel(GemmArgs g) {
     }
     MOE_LOAD(ra0, rb0, ia0, ib0, 0);
     MOE_LOAD(ra1, rb1, ia1, ib1, kof(1));
-    MOE_STORE(ra0, rb0, 0);
+    MOE_STORE(ra0, rb0, 0, 0);
     MOE_LOAD(ra0, rb0, ia0, ib0, kof(2));
     if constexpr (EPI == EPI_DSWIGLU) {
       for (int r = tid; r < BM; r += NT)
@@ -363,11 +371,11 @@ void gemm_bf16_kernel(GemmArgs g) {
     // the set being stored (loaded two tiles earlier), not the set loaded after it
     for (; kt + 4 < nk; kt += 2) {
       MOE_COMPUTE(0);  // tile kt
-      MOE_STORE(ra1, rb1, 1);
+      MOE_STORE(ra1, rb1, 1, kt + 1);
       MOE_LOAD(ra1, rb1, ia1, ib1, (kt + 3) * BK);
       __syncthreads();
       MOE_COMPUTE(1);  // tile kt+1
-      MOE_STORE(ra0, rb0, 0);
+      MOE_STORE(ra0, rb0, 0, kt + 2);
       MOE_LOAD(ra0, rb0, ia0, ib0, (kt + 4) * BK);
       __syncthreads();
     }
@@ -375,14 +383,14 @@ void gemm_bf16_kernel(GemmArgs g) {
     for (; kt < nk; kt += 2) {
       MOE_COMPUTE(0);
       if (kt + 1 < nk) {
-        MOE_STORE(ra1, rb1, 1);
+        MOE_STORE(ra1, rb1, 1, kt + 1);
         if (kt + 3 < nk) MOE_LOAD(ra1, rb1, ia1, ib1, (kt + 3) * BK);
       }
       __syncthreads();
       if (kt + 1 < nk) {
         MOE_COMPUTE(1);
         if (kt + 2 < nk) {
-          MOE_STORE(ra0, rb0, 0);
+          MOE_STORE(ra0, rb0, 0, kt + 2);
           if (kt + 4 < nk) MOE_LOAD(ra0, rb0, ia0, ib0, (kt + 4) * BK);
         }
         __syncthreads();
@@ -573,11 +581,11 @@ void gemm_bf16_kernel(GemmArgs g) {
   }
 }
 
-template <int MODE, bool A_KC, bool B_KC, int EPI>
+template <int MODE, bool A_KC, bool B_KC, int EPI, int GA = 0>
 hipError_t launch_tiles(int bm, int bn, int bk, int grid, const GemmArgs &g, hipStream_t st) {
 #define MOE_LAUNCH(BM_, BN_, BK_, WGM_, WGN_)                                                \
   if (bm == BM_ && bn == BN_ && bk == BK_) {                                              \
-    hipLaunchKernelGGL((gemm_bf16_kernel<MODE, A_KC, B_KC, EPI, BM_, BN_, BK_, WGM_, WGN_>), \
+    hipLaunchKernelGGL((gemm_bf16_kernel<MODE, A_KC, B_KC, EPI, BM_, BN_, BK_, WGM_, WGN_, GA>), \
                        dim3(grid), dim3(64 * WGM_ * WGN_), 0, st, g);                    \
     return hipGetLastError();                                                             \
   }
@@ -653,7 +661,13 @@ hipError_t launch_gemm_bf16(GemmKind kind, const GemmArgs &g, hipStream_t st) {
     case kUpBwd:
       return launch_tiles<GROUPED_M, true, true, EPI_STORE>(bm, bn, bk, grid, g, st);
     case kWeightGrad:
-      return launch_tiles<VARLEN_K, false, false, EPI_STORE>(bm, bn, bk, grid, g, st);
+      // the gathered operand is a compile-time choice: the row-index loads of the loop
+      // then carry no condition
+      if (g.a_rows && g.b_rows)
+        return launch_tiles<VARLEN_K, false, false, EPI_STORE, 3>(bm, bn, bk, grid, g, st);
+      if (g.a_rows) return launch_tiles<VARLEN_K, false, false, EPI_STORE, 1>(bm, bn, bk, grid, g, st);
+      if (g.b_rows) return launch_tiles<VARLEN_K, false, false, EPI_STORE, 2>(bm, bn, bk, grid, g, st);
+      return launch_tiles<VARLEN_K, false, false, EPI_STORE, 0>(bm, bn, bk, grid, g, st);
     default:
       return hipErrorInvalidValue;
   }
