@@ -418,7 +418,9 @@ void gemm_bf16_kernel(GemmArgs g) {
         for (int r = 0; r < 16; r += 2) {
           // even lane keeps row r and receives (row r, col+1); odd lane keeps row r+1
           const float send = odd ? acc[mi][ni][r] : acc[mi][ni][r + 1];
-          const float recv = __shfl_xor(send, 1, kWave);
+          // quad_perm [1,0,3,2]: exchange with the adjacent lane (no LDS traffic)
+          const float recv = __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(
+              0, (int)__float_as_uint(send), 0xB1, 0xF, 0xF, false));
           const int rr = odd ? r + 1 : r;
           const int row = wm * WM + mi * 32 + (rr >> 2) * 8 + (lane >> 5) * 4 + (rr & 3);
           const int col = wn * WN + ni * 32 + (col_l & ~1);
@@ -566,7 +568,8 @@ void gemm_bf16_kernel(GemmArgs g) {
           part[i] = keep + __shfl_xor(send, o, kWave);
         }
       }
-      const float rsum = part[0] + __shfl_xor(part[0], 1, kWave);
+      const float rsum = part[0] + __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(
+                                       0, (int)__float_as_uint(part[0]), 0xB1, 0xF, 0xF, false));
       const int rr = (lane & 31) >> 1;
       const int row = wm * WM + mi * 32 + (rr >> 2) * 8 + (lane >> 5) * 4 + (rr & 3);
       if ((lane & 1) == 0) red[wn * BM + row] = rsum;
