@@ -100,10 +100,10 @@ def test_bad_expert_ids_set_status():
         assert np.array_equal(bad[k], got[k]), k
 
 
-@pytest.mark.parametrize("N,K,E", [(300000, 8, 64), (1100000, 1, 7), (70000, 16, 1024)])
+@pytest.mark.parametrize("N,K,E", [(300000, 8, 64), (2200000, 1, 7), (140000, 16, 1024)])
 def test_long_columns_two_pass_scan(N, K, E):
-    """More than 2048 chunks of 512 slots: the column scan runs in segments (a pass of
-    segment sums, then the segments with their bases)."""
+    """More than 2048 chunks (of 1024 slots at these sizes): the column scan runs in
+    segments (a pass of segment sums, then the segments with their bases)."""
     rng = np.random.default_rng(N + K + E)
     idx = rng.integers(0, E, size=(N, K)).astype(np.int32)
     idx[rng.random((N, K)) < 0.25] = -1

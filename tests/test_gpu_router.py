@@ -111,7 +111,7 @@ def test_route_then_forward():
 
 
 def test_route_long_columns():
-    """Over 2048 metadata chunks: the counts and the aux loss's probability columns are
-    reduced in two passes."""
-    lg = synth.router_logits(150000, 64, seed=21)
+    """Over 2048 metadata chunks (of 1024 slots at this size): the counts and the aux
+    loss's probability columns are reduced in two passes."""
+    lg = synth.router_logits(300000, 64, seed=21)
     check(*run_route(lg, 8, 1, False))

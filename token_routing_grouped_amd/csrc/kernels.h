@@ -7,11 +7,11 @@ namespace moe {
 
 // ---- routing metadata -------------------------------------------------------
 constexpr int kMetaThreads = 256;
-#ifndef MOE_META_ITEMS
-#define MOE_META_ITEMS 2
-#endif
-constexpr int kMetaItems = MOE_META_ITEMS;              // slots per thread
-constexpr int kMetaChunk = kMetaThreads * kMetaItems;  // slots per workgroup
+// Slots per thread of the metadata kernels: 2 (chunks of 512 slots, enough workgroups
+// to fill the chip) below 2^20 slots, else 4 (chunks of 1024: longer runs per expert in
+// the sorted writes and fewer, shorter prefix columns; measured 84 -> 70 us at 2^23 slots).
+inline int meta_items(int64_t NK) { return NK >= ((int64_t)1 << 20) ? 4 : 2; }
+inline int meta_chunk(int64_t NK) { return kMetaThreads * meta_items(NK); }
 
 struct MetaOut {
   int32_t *expert_frequency, *expert_frequency_offset, *x_gather_idx, *s_scatter_idx,
@@ -25,7 +25,8 @@ struct MetaOut {
 };
 
 inline int meta_blocks(int64_t NK) {
-  int64_t b = (NK + kMetaChunk - 1) / kMetaChunk;
+  const int c = meta_chunk(NK);
+  int64_t b = (NK + c - 1) / c;
   return b < 1 ? 1 : (int)b;
 }
 // metadata workspace, in int32 elements: per-chunk histogram columns [E+2][nblk],

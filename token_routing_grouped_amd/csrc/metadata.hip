@@ -7,7 +7,8 @@
 // token-major with ascending slot; the sort is a stable counting sort, so the
 // result is unique.
 //
-// The slots are cut into chunks of kMetaChunk; three kernels:
+// The slots are cut into chunks of kMetaThreads * ITEMS (ITEMS from the slot count);
+// three kernels:
 //  1. meta_hist: each workgroup counts its chunk per expert (LDS integer atomics),
 //     flags ids outside [-1,E) and counts its valid slots. Columns: E experts,
 //     the flag, the valid count; stored column-major [E+2][nblk].
@@ -27,22 +28,24 @@
 
 namespace moe {
 
+template <int ITEMS>
 __global__ __launch_bounds__(kMetaThreads) void meta_hist_kernel(const int32_t *__restrict__ idx,
                                                                  int64_t NK, int E,
                                                                  int32_t *__restrict__ hist) {
+  constexpr int CHUNK = kMetaThreads * ITEMS;
   extern __shared__ int32_t sh[];  // [E+2]: counts, bad-id flag, valid count
   for (int e = threadIdx.x; e < E + 2; e += kMetaThreads) sh[e] = 0;
   __syncthreads();
-  const int64_t base = (int64_t)blockIdx.x * kMetaChunk + threadIdx.x;
-  int v[kMetaItems];
+  const int64_t base = (int64_t)blockIdx.x * CHUNK + threadIdx.x;
+  int v[ITEMS];
 #pragma unroll
-  for (int i = 0; i < kMetaItems; i++) {
+  for (int i = 0; i < ITEMS; i++) {
     const int64_t j = base + (int64_t)i * kMetaThreads;
     v[i] = j < NK ? idx[j] : -1;
   }
   int bad = 0, nvalid = 0;
 #pragma unroll
-  for (int i = 0; i < kMetaItems; i++) {
+  for (int i = 0; i < ITEMS; i++) {
     const bool ok = (unsigned)v[i] < (unsigned)E;
     if (ok)
       atomicAdd(&sh[v[i]], 1);
@@ -147,16 +150,22 @@ __global__ __launch_bounds__(kMetaThreads) void meta_scan_kernel(
   if (tid == 0 && seg == nseg - 1) tot[c] = s_base + t;
 }
 
+template <int ITEMS>
 __global__ __launch_bounds__(kMetaThreads) void meta_scatter_kernel(
     const int32_t *__restrict__ idx, const float *__restrict__ wts, int N, int K, int E,
     int nbits, int cap, const int32_t *__restrict__ pre, const int32_t *__restrict__ tot,
     MetaOut out) {
+  constexpr int CHUNK = kMetaThreads * ITEMS;
   extern __shared__ int32_t sh[];
   int32_t *s_off = sh;              // [E+2]: totals, scanned in place -> offsets, [E] = P,
                                     // [E+1] = bad-id flags
   int32_t *s_base = s_off + E + 2;  // [E+2]: this chunk's prefix row -> bases
   int32_t *s_run = s_base + E + 2;  // [4][E] per-wave running counts
   int32_t *s_misc = s_run + 4 * E;  // [8]: per-wave valid counts
+  int32_t *s_loc = s_misc + 8;      // [E+1]: this chunk's slots of experts < e (in-chunk)
+  int32_t *s_ps = s_loc + E + 1;    // [CHUNK] sorted position of the k-th sorted slot
+  int32_t *s_pt = s_ps + CHUNK;     // [CHUNK] its token
+  int32_t *s_pq = s_pt + CHUNK;     // [CHUNK] its pair index
   const int tid = threadIdx.x;
   const int w = tid / kWave;
   const int lane = tid % kWave;
@@ -174,18 +183,18 @@ __global__ __launch_bounds__(kMetaThreads) void meta_scatter_kernel(
 
   // this wave's slots (the w-th quarter of the chunk, rounds of 64), the chunk's
   // prefix row and the totals: all loads issued together
-  const int64_t wbase = (int64_t)me * kMetaChunk + (int64_t)w * (kMetaChunk / 4);
-  int r_e[kMetaItems];
-  float r_w[kMetaItems];
+  const int64_t wbase = (int64_t)me * CHUNK + (int64_t)w * (CHUNK / 4);
+  int r_e[ITEMS];
+  float r_w[ITEMS];
 #pragma unroll
-  for (int it = 0; it < kMetaItems; it++) {
+  for (int it = 0; it < ITEMS; it++) {
     const int64_t j = wbase + it * kWave + lane;
     r_e[it] = j < NK ? idx[j] : -1;
     r_w[it] = j < NK ? wts[j] : 0.0f;
   }
   const int32_t *prow = pre + (int64_t)me * W;
   const bool aux = me == 0 && out.aux;  // router: the load-balancing loss
-  float *s_prod = (float *)(s_misc + 8);  // [E] (router only)
+  float *s_prod = (float *)(s_pq + CHUNK);  // [E] (router only)
   for (int c = tid; c < W; c += kMetaThreads) {
     s_base[c] = prow[c];
     if (c <= E) {
@@ -220,11 +229,11 @@ __global__ __launch_bounds__(kMetaThreads) void meta_scatter_kernel(
   for (int e = tid; e < E; e += kMetaThreads) s_base[e] += s_off[e];  // base of this chunk
 
   // ---- stable in-chunk ranks
-  int r_rank[kMetaItems], r_vrank[kMetaItems];
+  int r_rank[ITEMS], r_vrank[ITEMS];
   int vrun = 0;
   int32_t *run = s_run + w * E;
 #pragma unroll
-  for (int it = 0; it < kMetaItems; it++) {
+  for (int it = 0; it < ITEMS; it++) {
     const int e = r_e[it];
     const bool v = (unsigned)e < (unsigned)E;
     const uint64_t vm = ballot64(v);
@@ -246,12 +255,23 @@ __global__ __launch_bounds__(kMetaThreads) void meta_scatter_kernel(
   }
   if (lane == 0) s_misc[w] = vrun;
   __syncthreads();
+  // From 2^18 slots the chunk's slots are staged in LDS in sorted order and leave as runs
+  // of consecutive sorted positions (coalesced writes; measured 20 % faster at 2^23
+  // slots); below, each lane writes its own slot's entries (0.5 us less at 2^17).
+  const bool staged = NK >= ((int64_t)1 << 18);
+  if (staged) {
+    for (int e = tid; e < E; e += kMetaThreads)
+      s_loc[e] = s_run[e] + s_run[E + e] + s_run[2 * E + e] + s_run[3 * E + e];
+    __syncthreads();
+    wave0_exclusive_scan(s_loc, E);  // s_loc[e] = in-chunk slots of experts < e, [E] = total
+    __syncthreads();
+  }
 
   int vbase = valid_before;
   for (int w2 = 0; w2 < w; w2++) vbase += s_misc[w2];
   const bool small = NK <= 0x7fffffff;
 #pragma unroll
-  for (int it = 0; it < kMetaItems; it++) {
+  for (int it = 0; it < ITEMS; it++) {
     const int64_t j = wbase + it * kWave + lane;
     if (j >= NK) break;
     const int q = vbase + r_vrank[it];  // valid slots before slot j
@@ -259,9 +279,15 @@ __global__ __launch_bounds__(kMetaThreads) void meta_scatter_kernel(
     if (j - (int64_t)t * K == 0) out.tok_off[t] = q;
     const int e = r_e[it];
     if (e < 0) continue;
-    int s = s_base[e] + r_rank[it];
-    for (int w2 = 0; w2 < w; w2++) s += s_run[w2 * E + e];
-    if ((unsigned)s < (unsigned)cap) {
+    int rk = r_rank[it];  // rank among this chunk's slots of expert e
+    for (int w2 = 0; w2 < w; w2++) rk += s_run[w2 * E + e];
+    const int s = s_base[e] + rk;
+    if (staged) {
+      const int pl = s_loc[e] + rk;  // in-chunk sorted position
+      s_ps[pl] = s;
+      s_pt[pl] = t;
+      s_pq[pl] = q;
+    } else if ((unsigned)s < (unsigned)cap) {
       out.x_gather_idx[s] = t;
       out.s_scatter_idx[s] = q;
     }
@@ -270,14 +296,29 @@ __global__ __launch_bounds__(kMetaThreads) void meta_scatter_kernel(
       out.router_scores[q] = r_w[it];
     }
   }
+  if (!staged) return;
+  __syncthreads();
+  const int nloc = s_loc[E];
+  for (int pl = tid; pl < nloc; pl += kMetaThreads) {
+    const int s = s_ps[pl];
+    if ((unsigned)s < (unsigned)cap) {
+      out.x_gather_idx[s] = s_pt[pl];
+      out.s_scatter_idx[s] = s_pq[pl];
+    }
+  }
 }
 
 hipError_t launch_meta_hist(const int32_t *topk_idx, int N, int K, int E, int32_t *ws,
                             hipStream_t stream) {
   const int64_t NK = (int64_t)N * K;
   const MetaWs L = meta_ws_layout(NK, E);
-  hipLaunchKernelGGL(meta_hist_kernel, dim3(L.nblk), dim3(kMetaThreads),
-                     (size_t)(E + 2) * sizeof(int32_t), stream, topk_idx, NK, E, ws + L.hist);
+  const size_t sh = (size_t)(E + 2) * sizeof(int32_t);
+  if (meta_items(NK) == 4)
+    hipLaunchKernelGGL(meta_hist_kernel<4>, dim3(L.nblk), dim3(kMetaThreads), sh, stream, topk_idx,
+                       NK, E, ws + L.hist);
+  else
+    hipLaunchKernelGGL(meta_hist_kernel<2>, dim3(L.nblk), dim3(kMetaThreads), sh, stream, topk_idx,
+                       NK, E, ws + L.hist);
   return hipGetLastError();
 }
 
@@ -302,12 +343,18 @@ hipError_t launch_meta_scan(int N, int K, int E, int32_t *ws, hipStream_t stream
 hipError_t launch_meta_scatter(const int32_t *topk_idx, const float *topk_weights, int N, int K,
                                int E, int capacity, const int32_t *ws, const MetaOut &out,
                                hipStream_t stream) {
-  const MetaWs L = meta_ws_layout((int64_t)N * K, E);
+  const int64_t NK = (int64_t)N * K;
+  const MetaWs L = meta_ws_layout(NK, E);
   int nbits = 0;
   while ((1 << nbits) < E) nbits++;
-  const size_t sh = (size_t)(2 * (E + 2) + 4 * E + 8 + (out.aux ? E : 0)) * sizeof(int32_t);
-  hipLaunchKernelGGL(meta_scatter_kernel, dim3(L.nblk), dim3(kMetaThreads), sh, stream, topk_idx,
-                     topk_weights, N, K, E, nbits, capacity, ws + L.pre, ws + L.tot, out);
+  const size_t sh = (size_t)(2 * (E + 2) + 4 * E + 8 + (E + 1) + 3 * meta_chunk(NK) +
+                             (out.aux ? E : 0)) * sizeof(int32_t);
+  if (meta_items(NK) == 4)
+    hipLaunchKernelGGL(meta_scatter_kernel<4>, dim3(L.nblk), dim3(kMetaThreads), sh, stream,
+                       topk_idx, topk_weights, N, K, E, nbits, capacity, ws + L.pre, ws + L.tot, out);
+  else
+    hipLaunchKernelGGL(meta_scatter_kernel<2>, dim3(L.nblk), dim3(kMetaThreads), sh, stream,
+                       topk_idx, topk_weights, N, K, E, nbits, capacity, ws + L.pre, ws + L.tot, out);
   return hipGetLastError();
 }
 

@@ -15,7 +15,7 @@
 // a whole wavefront per token; each lane holds NV (a power of two, from E) logits. The
 // K experts come from K rounds of two group reductions taken with DPP lane moves: the
 // maximum of the order-preserving logit bits, then the lowest expert id holding it, so
-// the choice is exact and deterministic. Each workgroup owns one chunk of kMetaChunk slots of the flattened
+// the choice is exact and deterministic. Each workgroup owns one metadata chunk of the flattened
 // [N,K] layout, exactly like the metadata histogram pass: it writes the slots of its
 // chunk (tokens straddling a chunk edge are evaluated by both workgroups, each writing
 // its own slots), counts them per expert into its histogram column, and sums the full
@@ -138,7 +138,7 @@ template <typename T, int LPT, int NV>
 __global__ __launch_bounds__(kRouteThreads) void route_hist_kernel(
     const T *__restrict__ logits, int N, int E, int K, int mode, int renorm, int want_p,
     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, int32_t *__restrict__ hist,
-    float *__restrict__ ppart) {
+    float *__restrict__ ppart, int chunk) {
   constexpr int TPW = kWave / LPT;                     // tokens per wave
   constexpr int NW = kRouteThreads / kWave;            // wavefronts per workgroup
   constexpr int TPB = TPW * NW;                        // tokens per workgroup round
@@ -152,8 +152,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_hist_kernel(
   __syncthreads();
 
   const int64_t NK = (int64_t)N * K;
-  const int64_t j0 = (int64_t)b * kMetaChunk;
-  const int64_t j1 = min(j0 + kMetaChunk, NK);  // this workgroup's slots [j0, j1)
+  const int64_t j0 = (int64_t)b * chunk;
+  const int64_t j1 = min(j0 + chunk, NK);  // this workgroup's slots [j0, j1)
   const int t0 = (int)(j0 / K), t1 = j1 > j0 ? (int)((j1 - 1) / K) : t0 - 1;
   float pacc[NV];
 #pragma unroll
@@ -280,7 +280,7 @@ hipError_t launch_route_hist(const void *logits, bool bf16, int N, int E, int K,
 #define MOE_ROUTE(T, LPT, NV)                                                              \
   hipLaunchKernelGGL((route_hist_kernel<T, LPT, NV>), dim3(L.nblk), dim3(kRouteThreads), sh, \
                      stream, (const T *)logits, N, E, K, mode, renorm, (int)want_p, topk_idx, \
-                     topk_w, meta_ws + L.hist, ppart)
+                     topk_w, meta_ws + L.hist, ppart, meta_chunk((int64_t)N * K))
 #define MOE_ROUTE_NV(T, LPT)                                                               \
   switch (nv) {                                                                            \
     case 1: MOE_ROUTE(T, LPT, 1); break;                                                   \
