@@ -109,3 +109,29 @@ def test_long_columns_two_pass_scan(N, K, E):
     idx[rng.random((N, K)) < 0.25] = -1
     w = rng.standard_normal((N, K)).astype(np.float32)
     check(idx, w, E)
+
+
+@pytest.mark.parametrize("NK", [(1 << 18) - 1, 1 << 18, (1 << 18) + 1,
+                                (1 << 20) - 1, 1 << 20, (1 << 20) + 1])
+def test_slot_count_thresholds(NK):
+    """Either side of the slot counts where the scatter starts staging its sorted writes
+    in LDS (2^18) and where the chunks grow from 512 to 1024 slots (2^20); K = 1 so that
+    every slot count is reachable, with a ragged last chunk."""
+    rng = np.random.default_rng(NK)
+    E = 48
+    idx = rng.integers(0, E, size=(NK, 1)).astype(np.int32)
+    idx[rng.random((NK, 1)) < 0.2] = -1
+    w = rng.standard_normal((NK, 1)).astype(np.float32)
+    check(idx, w, E)
+
+
+@pytest.mark.parametrize("N,K", [(32768, 8), (131072, 8)])
+def test_slot_count_thresholds_wide_rows(N, K):
+    """The same thresholds reached with K = 8 slots per token (token offsets then come
+    from slots in the middle of chunks)."""
+    rng = np.random.default_rng(N + K)
+    E = 64
+    idx = rng.integers(0, E, size=(N, K)).astype(np.int32)
+    idx[rng.random((N, K)) < 0.2] = -1
+    w = rng.standard_normal((N, K)).astype(np.float32)
+    check(idx, w, E)

@@ -115,3 +115,11 @@ def test_route_long_columns():
     loss's probability columns are reduced in two passes."""
     lg = synth.router_logits(300000, 64, seed=21)
     check(*run_route(lg, 8, 1, False))
+
+
+@pytest.mark.parametrize("N,K", [(32768, 8), (131072, 8), (262143, 4)])
+def test_route_slot_count_thresholds(N, K):
+    """Router at the slot counts where the metadata chunks and the scatter's write-out
+    change (2^18 and 2^20 slots), and a ragged last chunk."""
+    lg = synth.router_logits(N, 32, seed=N + K)
+    check(*run_route(lg, K, 1, True))
