@@ -11,8 +11,8 @@
 // over tokens of the full softmax at e (the usual load-balancing product form; the page
 // gives no formula).
 //
-// route_hist: 16 lanes per token (E <= 256, K <= 16; four tokens per wavefront), else
-// a whole wavefront per token; each lane holds NV (a power of two, from E) logits. The
+// route_hist: 8 lanes per token (E <= 128, K <= 8; eight tokens per wavefront), 16
+// (E <= 256, K <= 16; four tokens per wavefront), else a whole wavefront per token; each lane holds NV (a power of two, from E) logits. The
 // K experts come from K rounds of two group reductions taken with DPP lane moves: the
 // maximum of the order-preserving logit bits, then the lowest expert id holding it, so
 // the choice is exact and deterministic. Each workgroup owns one metadata chunk of the flattened
@@ -48,8 +48,9 @@ __device__ __forceinline__ float unordered(uint32_t k) {
 }
 
 // Reductions over the LPT lanes that share a token, with DPP lane moves (no LDS).
-// LPT = 16: one DPP row per token; rotations by 1, 2, 4, 8 give every lane of the
-// row the row's result. LPT = 64: Hillis-Steele shifts inside rows, then rows
+// LPT = 8: half a DPP row per token; pairwise exchanges (xor 1, xor 2, mirrored
+// halves) give every lane the group's result. LPT = 16: one DPP row per token;
+// rotations by 1, 2, 4, 8 give every lane of the row the row's result. LPT = 64: Hillis-Steele shifts inside rows, then rows
 // combined with row_bcast:15 / row_bcast:31; lane 63 holds the result, read back to
 // every lane. Max results are exact; a sum is taken from one lane, so every lane of a
 // token uses the same value.
@@ -61,7 +62,12 @@ template <int LPT>
 __device__ __forceinline__ float group_max_f32(float v) {
   const uint32_t NEG_INF = 0xff800000u;
 #define MOE_STEP(C, R, B) v = fmaxf(v, __uint_as_float(dpp<C, R, B>(NEG_INF, __float_as_uint(v))));
-  if constexpr (LPT == 16) {
+  if constexpr (LPT == 8) {
+    MOE_STEP(0xB1, 0xf, false)   // quad_perm [1,0,3,2]
+    MOE_STEP(0x4E, 0xf, false)   // quad_perm [2,3,0,1]
+    MOE_STEP(0x141, 0xf, false)  // row_half_mirror
+    return v;
+  } else if constexpr (LPT == 16) {
     MOE_STEP(0x121, 0xf, false)
     MOE_STEP(0x122, 0xf, false)
     MOE_STEP(0x124, 0xf, false)
@@ -89,7 +95,12 @@ __device__ __forceinline__ uint32_t group_ext_u32(uint32_t v) {
     const uint32_t o_ = dpp<C, R, B>(ID, v);                                    \
     v = MAX ? (o_ > v ? o_ : v) : (o_ < v ? o_ : v);                            \
   }
-  if constexpr (LPT == 16) {
+  if constexpr (LPT == 8) {
+    MOE_STEP(0xB1, 0xf, false)
+    MOE_STEP(0x4E, 0xf, false)
+    MOE_STEP(0x141, 0xf, false)
+    return v;
+  } else if constexpr (LPT == 16) {
     MOE_STEP(0x121, 0xf, false)
     MOE_STEP(0x122, 0xf, false)
     MOE_STEP(0x124, 0xf, false)
@@ -110,7 +121,14 @@ __device__ __forceinline__ uint32_t group_ext_u32(uint32_t v) {
 template <int LPT>
 __device__ __forceinline__ float group_sum_f32(float v) {
 #define MOE_STEP(C, R, B) v += __uint_as_float(dpp<C, R, B>(0u, __float_as_uint(v)));
-  if constexpr (LPT == 16) {
+  if constexpr (LPT == 8) {
+    // lanes exchange pairwise (xor 1, xor 2, then mirrored halves), so every lane adds
+    // the same two operands at every step: the eight results are bit-identical
+    MOE_STEP(0xB1, 0xf, false)
+    MOE_STEP(0x4E, 0xf, false)
+    MOE_STEP(0x141, 0xf, false)
+    return v;
+  } else if constexpr (LPT == 16) {
     MOE_STEP(0x121, 0xf, false)
     MOE_STEP(0x122, 0xf, false)
     MOE_STEP(0x124, 0xf, false)
@@ -131,7 +149,7 @@ __device__ __forceinline__ float group_sum_f32(float v) {
 // sum over the whole wave, the same value in every lane
 __device__ __forceinline__ float wave_sum_f32(float v) { return group_sum_f32<64>(v); }
 
-// LPT lanes per token (16: E <= 256 and K <= 16, four tokens per wave; else 64), NV
+// LPT lanes per token (8: E <= 128 and K <= 8; 16: E <= 256 and K <= 16; else 64), NV
 // logits per lane. Lane s of a token's group holds experts s, s+LPT, ...; after the
 // selection, lane k of the group holds the k-th expert.
 template <typename T, int LPT, int NV>
@@ -273,8 +291,11 @@ hipError_t launch_route_hist(const void *logits, bool bf16, int N, int E, int K,
   const MetaWs L = meta_ws_layout((int64_t)N * K, E);
   const size_t sh = (size_t)(E + 2) * sizeof(int32_t) +
                     (size_t)(kRouteThreads / kWave) * E * sizeof(float);
-  const bool narrow = E <= 16 * kMaxPerLane && K <= 16;  // 16 lanes per token
-  const int lpt = narrow ? 16 : kWave;
+  // 8 lanes per token when E <= 128 and K <= 8 (the K selected experts end on lanes
+  // 0..K-1); 16 when E <= 256 and K <= 16; else a whole wavefront
+  const bool eighth = E <= 8 * kMaxPerLane && K <= 8;
+  const bool narrow = E <= 16 * kMaxPerLane && K <= 16;
+  const int lpt = eighth ? 8 : narrow ? 16 : kWave;
   const int need = (E + lpt - 1) / lpt;  // logits per lane, rounded up to a power of two
   const int nv = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 16;
 #define MOE_ROUTE(T, LPT, NV)                                                              \
@@ -290,9 +311,13 @@ hipError_t launch_route_hist(const void *logits, bool bf16, int N, int E, int K,
     default: MOE_ROUTE(T, LPT, 16); break;                                                 \
   }
   if (bf16) {
-    if (narrow) { MOE_ROUTE_NV(uint16_t, 16) } else { MOE_ROUTE_NV(uint16_t, 64) }
+    if (eighth) { MOE_ROUTE_NV(uint16_t, 8) }
+    else if (narrow) { MOE_ROUTE_NV(uint16_t, 16) }
+    else { MOE_ROUTE_NV(uint16_t, 64) }
   } else {
-    if (narrow) { MOE_ROUTE_NV(float, 16) } else { MOE_ROUTE_NV(float, 64) }
+    if (eighth) { MOE_ROUTE_NV(float, 8) }
+    else if (narrow) { MOE_ROUTE_NV(float, 16) }
+    else { MOE_ROUTE_NV(float, 64) }
   }
 #undef MOE_ROUTE_NV
 #undef MOE_ROUTE
