@@ -26,8 +26,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   __bf16 h = (__bf16)f;
   return __builtin_bit_cast(uint16_t, h);
 }
+// two fp32 -> packed bf16 pair (lo in bits 0-15), round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 __device__ __forceinline__ int lane_id() {
@@ -99,5 +103,12 @@ __device__ __forceinline__ int xcd_chunked(int b, int G) {
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 __device__ __forceinline__ float sigmoid_f(float g) { return 1.0f / (1.0f + __expf(-g)); }
+// bf16 epilogues: the quotient by the hardware reciprocal (v_rcp_f32, about 1 ulp),
+// far below the bf16 rounding that follows. At g = -inf both forms give NaN; for any
+// finite g the reciprocal of an infinite 1 + e^-g is 0, as with the division.
+__device__ __forceinline__ float sigmoid_fast(float g) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
+__device__ __forceinline__ float silu_fast(float g) { return g * sigmoid_fast(g); }
 
 }  // namespace moe
