@@ -97,7 +97,7 @@ void gemm_bf16_kernel(GemmArgs g) {
   constexpr int WM = BM / WGM, WN = BN / WGN;  // wave tile
   constexpr int TM = WM / 32, TN = WN / 32;    // 32x32 sub-tiles per wave
   constexpr bool SWI = EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_CAT;
-  static_assert(TM >= 1 && TN >= 1 && (!SWI || TN % 2 == 0), "wave tile");
+  static_assert(TM >= 1 && TN >= 1 && (EPI != EPI_SWIGLU_CAT || TN % 2 == 0), "wave tile");
   using AS = TileShape<A_KC, BM, BK>;
   using BS = TileShape<B_KC, BN, BK>;
   constexpr int CPK = BK / 8;  // 16-byte chunks per row of a reduction-contiguous tile
@@ -205,7 +205,7 @@ void gemm_bf16_kernel(GemmArgs g) {
         int64_t col = (int64_t)nt * BN + (tid % CPR) * 8;
         if constexpr (EPI == EPI_SWIGLU_CAT) {
           // LDS chunk -> the gate or up columns it holds in the per-wave [gates | ups]
-          // order the SwiGLU epilogue reads (see the stage store of EPI_SWIGLU)
+          // order the concatenated-layout SwiGLU epilogue reads
           static_assert((WN / 2) % 8 == 0, "gate/up halves in whole chunks");
           const int c = (tid % CPR) * 8, w = c / WN, cw = c % WN;
           const int jb = nt * (BN / 2) + w * (WN / 2);
@@ -291,22 +291,7 @@ void gemm_bf16_kernel(GemmArgs g) {
         constexpr int CPB = BN / 8;                                                        \
         const int kr = tid / CPB + (NT / CPB) * i;                                         \
         const int nc = tid % CPB;                                                          \
-        if constexpr (EPI == EPI_SWIGLU) {                                                 \
-          /* interleaved (gate_j, up_j) columns -> per wave: its gates, then its ups */    \
-          const int half = (nc * 8) / WN;                                                  \
-          const int p0 = 4 * (nc % (WN / 8));                                              \
-          const int base = kr * BS::ld + half * WN + p0;                                   \
-          const u32x4 v = rb[i];                                                           \
-          u32x2 gate, up;                                                                  \
-          gate.x = (v.x & 0xffffu) | (v.y << 16);                                          \
-          gate.y = (v.z & 0xffffu) | (v.w << 16);                                          \
-          up.x = (v.x >> 16) | (v.y & 0xffff0000u);                                        \
-          up.y = (v.z >> 16) | (v.w & 0xffff0000u);                                        \
-          *(u32x2 *)(Bs_ + base) = gate;                                                   \
-          *(u32x2 *)(Bs_ + base + WN / 2) = up;                                            \
-        } else {                                                                           \
-          *(u32x4 *)(Bs_ + kr * BS::ld + nc * 8) = rb[i];                                  \
-        }                                                                                  \
+        *(u32x4 *)(Bs_ + kr * BS::ld + nc * 8) = rb[i];                                    \
       }                                                                                    \
     }                                                                                      \
   } while (0)
@@ -388,10 +373,10 @@ void gemm_bf16_kernel(GemmArgs g) {
   // Every load of the prologue and of the steady loop is unconditional (k offsets of
   // grouped-M are clamped to the last tile, varlen-K rows past the segment read as
   // zeros), so the memory wait counters stay exact across the loop.
-  // The ping-pong schedule below is taken for the down projection (plain store,
-  // n-contiguous weights) with eight waves: measured 6-7% faster there at every
-  // workload size, while the other grouped GEMMs tie or lose with it.
-  constexpr bool PP = MODE == GROUPED_M && EPI == EPI_STORE && !B_KC && WGM * WGN == 8;
+  // The ping-pong schedule below is taken by the eight-wave grouped GEMMs whose
+  // weights are n-contiguous (the up and down projections, B read by transposing LDS
+  // reads): measured 6-10% faster there; the backward GEMMs tie or lose with it.
+  constexpr bool PP = MODE == GROUPED_M && !B_KC && WGM * WGN == 8;
   if (PP && nk > 0) {
     // Waves 0-3 and 4-7 (one of each per SIMD) run half an iteration apart: between
     // two barriers one group multiplies tile j while the other reads tile j's
@@ -546,26 +531,50 @@ void gemm_bf16_kernel(GemmArgs g) {
   } else if constexpr (SWI) {
     // Both outputs are staged through LDS and leave as whole rows of 16-byte streaming
     // stores: h (interleaved (gate, up) pairs, [BM][BN]) first, then a ([BM][BN/2]).
-    // The W_up tile was split per wave into gates and ups, so acc[.][np] holds gates
-    // and acc[.][np + TN/2] the matching ups.
     constexpr int HLD = BN + 8, ALD = BN / 2 + 8;  // staging row strides (elements)
     static_assert(BM * HLD <= SMEM && BM * ALD <= SMEM, "staging tiles fit");
     uint16_t *Hst = smem;
     uint16_t *Hs = (uint16_t *)g.C;  // may be null (inference); always interleaved
     uint16_t *Aout = (uint16_t *)g.C2;
+    const bool odd = lane & 1;
     // (gate, up) of one row and pair -> f(tile row, local pair, gate, up)
     auto for_pairs = [&](auto &&f) {
+      if constexpr (EPI == EPI_SWIGLU) {
+        // Interleaved W_up columns: even accumulator columns are gates, odd ones the
+        // matching ups. As in the plain-store epilogue, a quad_perm [1,0,3,2] move
+        // gives the even lane of a pair (gate, up) of row r and the odd lane that of
+        // row r+1.
 #pragma unroll
-      for (int mi = 0; mi < TM; mi++)
+        for (int mi = 0; mi < TM; mi++)
 #pragma unroll
-        for (int np = 0; np < TN / 2; np++) {
-          const int jl = wn * (WN / 2) + np * 32 + col_l;
+          for (int ni = 0; ni < TN; ni++) {
+            const int jl = (wn * WN + ni * 32 + (col_l & ~1)) / 2;
 #pragma unroll
-          for (int r = 0; r < 16; r++) {
-            const int row = wm * WM + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-            f(row, jl, acc[mi][np][r], acc[mi][np + TN / 2][r]);
+            for (int r = 0; r < 16; r += 2) {
+              const float a0 = acc[mi][ni][r], a1 = acc[mi][ni][r + 1];
+              const float n0 = __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp(
+                  (int)__float_as_uint(a0), 0xB1, 0xF, 0xF, false));
+              const float n1 = __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp(
+                  (int)__float_as_uint(a1), 0xB1, 0xF, 0xF, false));
+              const int row = wm * WM + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3) + odd;
+              f(row, jl, odd ? n1 : a0, odd ? a1 : n0);
+            }
           }
-        }
+      } else {
+        // concatenated W_up: the B tile holds per wave its gates, then its ups, so
+        // acc[.][np] holds gates and acc[.][np + TN/2] the matching ups
+#pragma unroll
+        for (int mi = 0; mi < TM; mi++)
+#pragma unroll
+          for (int np = 0; np < TN / 2; np++) {
+            const int jl = wn * (WN / 2) + np * 32 + col_l;
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+              const int row = wm * WM + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+              f(row, jl, acc[mi][np][r], acc[mi][np + TN / 2][r]);
+            }
+          }
+      }
     };
     if (Hs) {
       for_pairs([&](int row, int jl, float gt, float up) {
