@@ -111,37 +111,56 @@ void gemm_bf16_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM];
   // EPI_DSWIGLU: router weight of every tile row, fetched while the main loop starts
   __shared__ __attribute__((aligned(16))) float s_wq[EPI == EPI_DSWIGLU ? BM : 4];
-  int *s_pref = (int *)smem;  // expert tile table, used before the first stage is written
+  // grouped-M: row tiles before each expert (prefix) and the expert offsets, built once
+  __shared__ int s_tab[MODE == GROUPED_M ? 2 * (MOE_MAX_EXPERTS + 1) : 1];
+  int *s_pref = s_tab, *s_off = s_tab + (MODE == GROUPED_M ? MOE_MAX_EXPERTS + 1 : 0);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WGN, wn = wave % WGN;
+  int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;  // re-derived per tile below
+  int wm = wave / WGN, wn = wave % WGN;
   const int P = g.foff[g.E];
   const uint16_t *A = (const uint16_t *)g.A;
   const uint16_t *B = (const uint16_t *)g.B;
 
-  int e, mt = 0, nt, row0 = 0, rows = 0, seg0 = 0, seglen = 0, nk;
-  if constexpr (MODE == GROUPED_M) {
-    if (P > g.cap) return;
-    for (int i = tid; i < g.E; i += NT) s_pref[i] = (g.foff[i + 1] - g.foff[i] + BM - 1) / BM;
-    __syncthreads();
-    wave0_exclusive_scan(s_pref, g.E);
-    __syncthreads();
-    const int ntn = g.N / BN;
-    const int G = s_pref[g.E] * ntn;
-    if ((int)blockIdx.x >= G) return;
-    const int L = xcd_chunked(blockIdx.x, G);
+  int e = 0, mt = 0, nt = 0, row0 = 0, rows = 0, seg0 = 0, seglen = 0, nk = 0;
+  // Grouped-M workgroups are persistent: XCD x (= blockIdx % 8, the hardware's
+  // round-robin) owns one contiguous run of the tiles, which its workgroups take in
+  // turn, so the tiles in flight on an XCD are neighbours (shared weights and rows in
+  // its L2). The grid is a multiple of 8 workgroups.
+  int tl = 0, tcnt = 0, tstart = 0, tstep = 1, ntn = 1;
+  auto decode = [&](int L, int &e_, int &nt_, int &row0_, int &rows_) {
     const int mtile = L / ntn;
-    nt = L - mtile * ntn;
+    nt_ = L - mtile * ntn;
     int lo = 0, hi = g.E - 1;  // largest e with s_pref[e] <= mtile
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (s_pref[mid] <= mtile) lo = mid; else hi = mid - 1;
     }
-    e = lo;
-    row0 = g.foff[e] + (mtile - s_pref[e]) * BM;
-    rows = min(BM, g.foff[e + 1] - row0);
+    // wave-uniform values, kept in scalar registers
+    e_ = __builtin_amdgcn_readfirstlane(lo);
+    nt_ = __builtin_amdgcn_readfirstlane(nt_);
+    row0_ = __builtin_amdgcn_readfirstlane(s_off[lo] + (mtile - s_pref[lo]) * BM);
+    rows_ = __builtin_amdgcn_readfirstlane(min(BM, s_off[lo + 1] - row0_));
+  };
+  if constexpr (MODE == GROUPED_M) {
+    if (P > g.cap) return;
+    for (int i = tid; i <= g.E; i += NT) {
+      const int o = g.foff[i];
+      s_off[i] = o;
+      if (i < g.E) s_pref[i] = (g.foff[i + 1] - o + BM - 1) / BM;
+    }
+    __syncthreads();
+    wave0_exclusive_scan(s_pref, g.E);
+    __syncthreads();
+    ntn = g.N / BN;
+    const int G = s_pref[g.E] * ntn;
+    const int x = blockIdx.x % kNumXcd, q = G / kNumXcd, rq = G % kNumXcd;
+    tstart = x * q + min(x, rq);
+    tcnt = q + (x < rq ? 1 : 0);
+    tl = blockIdx.x / kNumXcd;
+    tstep = gridDim.x / kNumXcd;
+    if (tl >= tcnt) return;
+    decode(tstart + tl, e, nt, row0, rows);
     nk = g.K / BK;
-    __syncthreads();  // the table's LDS is reused by the stages below
   } else {
     // Work per tile is the expert's row count, which can be very skewed. Experts are
     // taken largest first, and every XCD gets one contiguous eighth of each expert's
@@ -184,36 +203,45 @@ void gemm_bf16_kernel(GemmArgs g) {
   //  mn-contiguous tile of C cols: k-rows (tid / (C/8)) + (256/(C/8))*i, chunk tid % (C/8)
   const uint16_t *a_row[A_LD];
   const uint16_t *b_ptr[B_LD];
-  if constexpr (MODE == GROUPED_M) {
+  // pair position of A chunk row i of a tile; rows past the segment re-read the
+  // tile's first row: their accumulator rows are never stored, so need no zeroing
+  auto a_pos = [&](int i, int row0_, int rows_) {
+    const int r = tid / CPK + (NT / CPK) * i;
+    return row0_ + (r < rows_ ? r : 0);
+  };
+  // row pointers of a tile, from the memory rows of its A chunks
+  auto set_ptrs = [&](const int *arow, int e_, int nt_) {
 #pragma unroll
-    for (int i = 0; i < A_LD; i++) {
-      // rows past the segment re-read the tile's first row: their accumulator rows
-      // are never stored, so they need no zeroing
-      const int r = tid / CPK + (NT / CPK) * i;
-      const int s = row0 + (r < rows ? r : 0);
-      const int64_t gr = g.a_rows ? g.a_rows[s] : s;
-      a_row[i] = A + gr * g.lda + (tid % CPK) * 8;
-    }
+    for (int i = 0; i < A_LD; i++) a_row[i] = A + (int64_t)arow[i] * g.lda + (tid % CPK) * 8;
 #pragma unroll
     for (int i = 0; i < B_LD; i++) {
       if constexpr (B_KC) {
-        const int64_t n = (int64_t)nt * BN + tid / CPK + (NT / CPK) * i;
-        b_ptr[i] = B + (int64_t)e * g.b_es + n * g.ldb + (tid % CPK) * 8;
+        const int64_t n = (int64_t)nt_ * BN + tid / CPK + (NT / CPK) * i;
+        b_ptr[i] = B + (int64_t)e_ * g.b_es + n * g.ldb + (tid % CPK) * 8;
       } else {
         constexpr int CPR = BN / 8;  // chunks per k-row
         const int kr = tid / CPR + (NT / CPR) * i;
-        int64_t col = (int64_t)nt * BN + (tid % CPR) * 8;
+        int64_t col = (int64_t)nt_ * BN + (tid % CPR) * 8;
         if constexpr (EPI == EPI_SWIGLU_CAT) {
           // LDS chunk -> the gate or up columns it holds in the per-wave [gates | ups]
           // order the concatenated-layout SwiGLU epilogue reads
           static_assert((WN / 2) % 8 == 0, "gate/up halves in whole chunks");
           const int c = (tid % CPR) * 8, w = c / WN, cw = c % WN;
-          const int jb = nt * (BN / 2) + w * (WN / 2);
+          const int jb = nt_ * (BN / 2) + w * (WN / 2);
           col = cw < WN / 2 ? jb + cw : g.N / 2 + jb + (cw - WN / 2);
         }
-        b_ptr[i] = B + (int64_t)e * g.b_es + (int64_t)kr * g.ldb + col;
+        b_ptr[i] = B + (int64_t)e_ * g.b_es + (int64_t)kr * g.ldb + col;
       }
     }
+  };
+  int arow[A_LD];  // grouped-M: memory rows of the A chunks of the next tile
+  if constexpr (MODE == GROUPED_M) {
+#pragma unroll
+    for (int i = 0; i < A_LD; i++) {
+      const int s_ = a_pos(i, row0, rows);
+      arow[i] = (GA & 1) ? g.a_rows[s_] : s_;
+    }
+    set_ptrs(arow, e, nt);
   }
 
   // Register sets and LDS stages are handled by macros so every array index is a
@@ -358,13 +386,6 @@ void gemm_bf16_kernel(GemmArgs g) {
   } while (0)
 
   f32x16 acc[TM][TN];
-#pragma unroll
-  for (int mi = 0; mi < TM; mi++)
-#pragma unroll
-    for (int ni = 0; ni < TN; ni++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) acc[mi][ni][r] = 0.0f;
-
   // Two LDS stages and two register sets: the tile stored into a stage was loaded
   // from memory two tiles earlier, so each global load has about two tiles of MFMA
   // work to arrive.
@@ -377,18 +398,46 @@ void gemm_bf16_kernel(GemmArgs g) {
   // weights are n-contiguous (the up and down projections, B read by transposing LDS
   // reads): measured 6-10% faster there; the backward GEMMs tie or lose with it.
   constexpr bool PP = MODE == GROUPED_M && !B_KC && WGM * WGN == 8;
-  if (PP && nk > 0) {
-    // Waves 0-3 and 4-7 (one of each per SIMD) run half an iteration apart: between
-    // two barriers one group multiplies tile j while the other reads tile j's
-    // fragments, stores tile j+1 into the other stage and loads tile j+3. Two stages
-    // suffice: a stage is rewritten two phases after both groups have read it.
-    auto kof = [&](int t) { return (MODE == GROUPED_M ? min(t, nk - 1) : t) * BK; };
-    bf16x8 paf[BK / 16][TM], pbf[BK / 16][TN];
+  auto kof = [&](int t) { return (MODE == GROUPED_M ? min(t, nk - 1) : t) * BK; };
+  // Grouped-M: the first k-tile of every tile after a workgroup's first is loaded
+  // before the epilogue of the tile before it (one register set: the epilogues need
+  // the rest of the registers; the DSWIGLU epilogue needs all of them).
+  constexpr bool EARLY = MODE == GROUPED_M && EPI != EPI_DSWIGLU;
+  if constexpr (EARLY) MOE_LOAD(ra0, rb0, ia0, ib0, 0);
+  for (;;) {
+  // The thread index passes through an empty asm at every tile, so the addresses
+  // derived from it are recomputed per tile instead of being kept live (hoisted)
+  // across the tile loop, which would cost registers the main loop needs.
+  asm volatile("" : "+v"(tid));
+  lane = tid & 63;
+  wave = tid >> 6;
+  wm = wave / WGN;
+  wn = wave % WGN;
+#pragma unroll
+  for (int mi = 0; mi < TM; mi++)
+#pragma unroll
+    for (int ni = 0; ni < TN; ni++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[mi][ni][r] = 0.0f;
+  // grouped-M: the next tile of this workgroup (the last one again after the last,
+  // so the loads below stay unconditional); its A rows are fetched now and used
+  // after the main loop
+  const bool more = MODE == GROUPED_M && tl + tstep < tcnt;
+  int e_n = e, nt_n = nt, row0_n = row0, rows_n = rows;
+  if constexpr (MODE == GROUPED_M) {
+    decode(tstart + min(tl + tstep, tcnt - 1), e_n, nt_n, row0_n, rows_n);
+#pragma unroll
+    for (int i = 0; i < A_LD; i++) {
+      const int s_ = a_pos(i, row0_n, rows_n);
+      arow[i] = (GA & 1) ? g.a_rows[s_] : s_;
+    }
+  }
+  if (nk > 0) {
     if constexpr (MODE == VARLEN_K) {
       MOE_ROWS(ia0, ib0, 0);
       MOE_ROWS(ia1, ib1, BK);
     }
-    MOE_LOAD(ra0, rb0, ia0, ib0, 0);
+    if constexpr (!EARLY) MOE_LOAD(ra0, rb0, ia0, ib0, 0);
     MOE_LOAD(ra1, rb1, ia1, ib1, kof(1));
     MOE_STORE(ra0, rb0, 0, 0);
     MOE_LOAD(ra0, rb0, ia0, ib0, kof(2));
@@ -397,6 +446,13 @@ void gemm_bf16_kernel(GemmArgs g) {
         s_wq[r] = r < rows ? g.scores[g.s_scatter[row0 + r]] : 0.0f;
     }
     __syncthreads();
+  }
+  if (PP && nk > 0) {
+    // Waves 0-3 and 4-7 (one of each per SIMD) run half an iteration apart: between
+    // two barriers one group multiplies tile j while the other reads tile j's
+    // fragments, stores tile j+1 into the other stage and loads tile j+3. Two stages
+    // suffice: a stage is rewritten two phases after both groups have read it.
+    bf16x8 paf[BK / 16][TM], pbf[BK / 16][TN];
     const bool late = __builtin_amdgcn_readfirstlane(wave) >= 4;  // wave-uniform
     if (late) MOE_PP_BARRIER();
     int j = 0;
@@ -427,20 +483,6 @@ void gemm_bf16_kernel(GemmArgs g) {
     }
     if (!late) MOE_PP_BARRIER();
   } else if (nk > 0) {
-    auto kof = [&](int t) { return (MODE == GROUPED_M ? min(t, nk - 1) : t) * BK; };
-    if constexpr (MODE == VARLEN_K) {
-      MOE_ROWS(ia0, ib0, 0);
-      MOE_ROWS(ia1, ib1, BK);
-    }
-    MOE_LOAD(ra0, rb0, ia0, ib0, 0);
-    MOE_LOAD(ra1, rb1, ia1, ib1, kof(1));
-    MOE_STORE(ra0, rb0, 0, 0);
-    MOE_LOAD(ra0, rb0, ia0, ib0, kof(2));
-    if constexpr (EPI == EPI_DSWIGLU) {
-      for (int r = tid; r < BM; r += NT)
-        s_wq[r] = r < rows ? g.scores[g.s_scatter[row0 + r]] : 0.0f;
-    }
-    __syncthreads();
     int kt = 0;
     // steady state, free of branches: the wait before a stage store only holds back
     // the set being stored (loaded two tiles earlier), not the set loaded after it
@@ -471,6 +513,10 @@ void gemm_bf16_kernel(GemmArgs g) {
         __syncthreads();
       }
     }
+  }
+  if constexpr (MODE == GROUPED_M) {  // the next tile's rows (and first k-tile)
+    set_ptrs(arow, e_n, nt_n);
+    if constexpr (EARLY) MOE_LOAD(ra0, rb0, ia0, ib0, 0);
   }
 #undef MOE_LOAD
 #undef MOE_ROWS
@@ -515,10 +561,12 @@ void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < BM * CPR / NT; i++) {
       const int c = tid + NT * i;
-      const int row = c / CPR, ch = c % CPR;
+      // grouped-M rows past the segment store the segment's last row again (the same
+      // bytes): every store is issued, so the wait counters stay exact for the next
+      // tile's loads already in flight
+      const int row = MODE == GROUPED_M ? min(c / CPR, rows - 1) : c / CPR, ch = c % CPR;
       int64_t off;
       if constexpr (MODE == GROUPED_M) {
-        if (row >= rows) continue;
         off = (int64_t)(row0 + row) * g.ldc;
       } else {
         off = (int64_t)e * g.c_es + (int64_t)(mt * BM + row) * g.ldc;
@@ -584,11 +632,12 @@ void gemm_bf16_kernel(GemmArgs g) {
       constexpr int CPR = BN / 8;
 #pragma unroll
       for (int i = 0; i < BM * CPR / NT; i++) {
-        const int c = tid + NT * i, row = c / CPR, ch = c % CPR;
-        if (row < rows)
-          __builtin_nontemporal_store(*(const u32x4 *)(Hst + row * HLD + ch * 8),
-                                      (u32x4 *)(Hs + (int64_t)(row0 + row) * g.ldc +
-                                                (int64_t)nt * BN + ch * 8));
+        // rows past the segment store its last row again (the same bytes), so every
+        // store is issued and the wait counters stay exact
+        const int c = tid + NT * i, row = min(c / CPR, rows - 1), ch = c % CPR;
+        __builtin_nontemporal_store(*(const u32x4 *)(Hst + row * HLD + ch * 8),
+                                    (u32x4 *)(Hs + (int64_t)(row0 + row) * g.ldc +
+                                              (int64_t)nt * BN + ch * 8));
       }
       __syncthreads();
     }
@@ -599,9 +648,8 @@ void gemm_bf16_kernel(GemmArgs g) {
     constexpr int CPA = BN / 16;
 #pragma unroll
     for (int i = 0; i < BM * CPA / NT; i++) {
-      const int c = tid + NT * i, row = c / CPA, ch = c % CPA;
-      if (row < rows)
-        __builtin_nontemporal_store(*(const u32x4 *)(Hst + row * ALD + ch * 8),
+      const int c = tid + NT * i, row = min(c / CPA, rows - 1), ch = c % CPA;
+      __builtin_nontemporal_store(*(const u32x4 *)(Hst + row * ALD + ch * 8),
                                     (u32x4 *)(Aout + (int64_t)(row0 + row) * g.ldc2 +
                                               (int64_t)nt * (BN / 2) + ch * 8));
     }
@@ -687,14 +735,39 @@ void gemm_bf16_kernel(GemmArgs g) {
       g.partial[(int64_t)(row0 + r) * g.n_ntiles + nt] = v;
     }
   }
+  if (!more) break;
+  __syncthreads();  // the epilogue's LDS reads are done before the next stage stores
+  tl += tstep;
+  e = e_n;
+  nt = nt_n;
+  row0 = row0_n;
+  rows = rows_n;
+  }  // tiles
 }
 
 template <int MODE, bool A_KC, bool B_KC, int EPI, int GA = 0>
 hipError_t launch_tiles(int bm, int bn, int bk, int grid, const GemmArgs &g, hipStream_t st) {
+  // grouped-M workgroups are persistent: as many as the chip holds at once (capped
+  // by the tile count), rounded up to a multiple of the 8 XCDs
 #define MOE_LAUNCH(BM_, BN_, BK_, WGM_, WGN_)                                                \
   if (bm == BM_ && bn == BN_ && bk == BK_) {                                              \
-    hipLaunchKernelGGL((gemm_bf16_kernel<MODE, A_KC, B_KC, EPI, BM_, BN_, BK_, WGM_, WGN_, GA>), \
-                       dim3(grid), dim3(64 * WGM_ * WGN_), 0, st, g);                    \
+    auto kern = gemm_bf16_kernel<MODE, A_KC, B_KC, EPI, BM_, BN_, BK_, WGM_, WGN_, GA>;    \
+    int blocks = grid;                                                                    \
+    if constexpr (MODE == GROUPED_M) {                                                    \
+      static int occ = 0; /* workgroups per CU, a property of the kernel */               \
+      if (occ == 0 &&                                                                     \
+          hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, 64 * WGM_ * WGN_, 0) != \
+              hipSuccess)                                                                 \
+        return hipErrorInvalidValue;                                                      \
+      int dev = 0, ncu = 0;                                                               \
+      if (hipGetDevice(&dev) != hipSuccess ||                                             \
+          hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) !=      \
+              hipSuccess)                                                                 \
+        return hipErrorInvalidValue;                                                      \
+      const int64_t cap = (int64_t)ncu * (occ > 0 ? occ : 1);                             \
+      blocks = (int)(((grid < cap ? grid : cap) + kNumXcd - 1) / kNumXcd * kNumXcd);      \
+    }                                                                                     \
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * WGM_ * WGN_), 0, st, g);             \
     return hipGetLastError();                                                             \
   }
   if constexpr (MODE == GROUPED_M) {
@@ -758,16 +831,22 @@ hipError_t launch_gemm_bf16(GemmKind kind, const GemmArgs &g, hipStream_t st) {
   int bm, bn, bk;
   gemm_tile(kind, g, &bm, &bn, &bk);
   switch (kind) {
+    // grouped-M: GA = 1 when the A rows are gathered (x_gather_idx), a compile-time
+    // choice like the weight gradients' (the row loads then carry no condition)
     case kUpSwiGLU:
+      if (!g.a_rows) return hipErrorInvalidValue;
       if (g.gu_concat)
-        return launch_tiles<GROUPED_M, true, false, EPI_SWIGLU_CAT>(bm, bn, bk, grid, g, st);
-      return launch_tiles<GROUPED_M, true, false, EPI_SWIGLU>(bm, bn, bk, grid, g, st);
+        return launch_tiles<GROUPED_M, true, false, EPI_SWIGLU_CAT, 1>(bm, bn, bk, grid, g, st);
+      return launch_tiles<GROUPED_M, true, false, EPI_SWIGLU, 1>(bm, bn, bk, grid, g, st);
     case kDown:
-      return launch_tiles<GROUPED_M, true, false, EPI_STORE>(bm, bn, bk, grid, g, st);
+      if (g.a_rows) return hipErrorInvalidValue;
+      return launch_tiles<GROUPED_M, true, false, EPI_STORE, 0>(bm, bn, bk, grid, g, st);
     case kDownBwd:
-      return launch_tiles<GROUPED_M, true, true, EPI_DSWIGLU>(bm, bn, bk, grid, g, st);
+      if (!g.a_rows) return hipErrorInvalidValue;
+      return launch_tiles<GROUPED_M, true, true, EPI_DSWIGLU, 1>(bm, bn, bk, grid, g, st);
     case kUpBwd:
-      return launch_tiles<GROUPED_M, true, true, EPI_STORE>(bm, bn, bk, grid, g, st);
+      if (g.a_rows) return hipErrorInvalidValue;
+      return launch_tiles<GROUPED_M, true, true, EPI_STORE, 0>(bm, bn, bk, grid, g, st);
     case kWeightGrad:
       // the gathered operand is a compile-time choice: the row-index loads of the loop
       // then carry no condition
