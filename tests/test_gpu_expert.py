@@ -74,6 +74,14 @@ def test_exact_tile_boundaries():
     assert np.all(np64(g.dw_up)[0] == 0) and np.all(np64(g.dw_down)[0] == 0)
 
 
+def test_more_tiles_than_workgroups():
+    """~9000 rows per expert: every grouped GEMM has more 256-row tiles than the chip holds
+    workgroups at once, so each persistent workgroup walks several tiles (next-tile loads
+    issued before an epilogue), each expert ending in a ragged tile."""
+    d = synth.case(N=10000, H=256, I=256, E=8, K=8, seed=7, p_invalid=0.1)
+    run_case(d)
+
+
 def test_duplicate_experts_in_a_row_and_empty_rows():
     rng = np.random.default_rng(5)
     idx = rng.integers(0, 3, size=(200, 4)).astype(np.int32)
