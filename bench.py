@@ -74,6 +74,43 @@ def counted_traffic(kernel: str, workload: str):
     return ent.get("bytes_per_launch")
 
 
+class TimingEvent:
+    """A HIP event for timing only (hipEventDisableSystemFence): recording it does not
+    write back and invalidate the caches, which with default events opened a ~6 us gap
+    before and after the bracketed kernel. Same interface as torch.cuda.Event for
+    moe_time_kernel (cuda_event) and for reading (elapsed_time, in ms)."""
+    _hip = None
+
+    def __init__(self):
+        import ctypes
+        if TimingEvent._hip is None:
+            try:
+                TimingEvent._hip = ctypes.CDLL("libamdhip64.so")
+            except OSError:
+                TimingEvent._hip = ctypes.CDLL("/opt/rocm/lib/libamdhip64.so")
+        self._ct = ctypes
+        h = ctypes.c_void_p()
+        rc = TimingEvent._hip.hipEventCreateWithFlags(ctypes.byref(h), ctypes.c_uint(0x20000000))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        self.cuda_event = h.value
+
+    def elapsed_time(self, end) -> float:
+        ms = self._ct.c_float(0.0)
+        rc = TimingEvent._hip.hipEventElapsedTime(self._ct.byref(ms), self._ct.c_void_p(self.cuda_event),
+                                                  self._ct.c_void_p(end.cuda_event))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        try:
+            if TimingEvent._hip is not None and getattr(self, "cuda_event", None):
+                TimingEvent._hip.hipEventDestroy(self._ct.c_void_p(self.cuda_event))
+        except Exception:  # interpreter shutdown
+            pass
+
+
 def cpu_baseline(d, backward: bool, target_s: float):
     """The oracle (fp64, OpenMP) on the first tokens of the workload: metadata,
     forward and (if the workload has it) backward, on full tensors of that sample."""
@@ -296,7 +333,7 @@ def main():
     kernels = step_kernels if backward else step_kernels[:step_kernels.index("combine") + 1]
     kernel_us = {}
     for k in kernels:
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        ev = [TimingEvent() for _ in range(6)]
         moe.moe_time_kernel(k, ev)
         for _ in range(3):
             step()
@@ -337,7 +374,7 @@ def main():
     meta_bytes = 8 * N * K + 16 * P + 4 * (N + 1) + 4 * E + 4 * (E + 1)
 
     # timed region: K steps, the dominant kernel bracketed on its stream
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    ev = [TimingEvent() for _ in range(2 * args.steps)]
     s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     moe.moe_time_kernel(dominant, ev)
