@@ -92,14 +92,6 @@ __device__ __forceinline__ void wave0_exclusive_scan(int *a, int n) {
   if (lane == kWave - 1) a[n] = incl;
 }
 
-// Bijection of hardware workgroup ids [0,G) onto logical ids so that each XCD
-// (hardware id modulo 8) receives one contiguous range of logical ids: work that
-// shares operands lands on the same L2.
-__device__ __forceinline__ int xcd_chunked(int b, int G) {
-  const int x = b % kNumXcd, i = b / kNumXcd;
-  const int q = G / kNumXcd, r = G % kNumXcd;
-  return x * q + (x < r ? x : r) + i;
-}
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 __device__ __forceinline__ float sigmoid_f(float g) { return 1.0f / (1.0f + __expf(-g)); }

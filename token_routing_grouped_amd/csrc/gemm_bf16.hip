@@ -5,26 +5,28 @@
 // one F.linear per expert because variable-size GEMMs cannot be batched there;
 // GitHub issue #68 keeps SonicMoE's grouped GEMM for the expert compute. Here one
 // launch covers every expert:
-//  - grouped-M: a workgroup owns a BMxBN output tile of one expert segment. It
-//    reads the segment offsets (expert_frequency_offset), counts ceil(freq_e/BM)
-//    row tiles per expert, and finds its (expert, first row, column tile) itself,
-//    so the grid is sized from the capacity alone and no host sync is needed;
-//    surplus workgroups exit. Partial row tiles are padded with zeros in LDS,
-//    never in memory. A rows are gathered through a row map (x_gather_idx)
-//    directly in the tile load.
+//  - grouped-M: a tile is a BMxBN output block of one expert segment. Each
+//    workgroup reads the segment offsets (expert_frequency_offset), counts
+//    ceil(freq_e/BM) row tiles per expert and finds the (expert, first row, column
+//    tile) of every tile it takes itself, so the launch needs no host sync. The
+//    workgroups are persistent (as many as the chip holds at once) and walk the
+//    tiles of their XCD. Partial row tiles are padded in LDS, never in memory. A
+//    rows are gathered through a row map (x_gather_idx) directly in the tile load.
 //  - varlen-K (weight gradients): a workgroup owns a BMxBN tile of one expert's
 //    gradient and reduces over that expert's rows; empty experts write zeros.
-// Workgroup ids are regrouped so that each of the 8 XCDs runs a contiguous run
-// of tiles (tiles of one expert share weights, consecutive column tiles share the
-// gathered rows), which keeps the reuse inside one L2.
+// Each of the 8 XCDs runs a contiguous run of tiles (tiles of one expert share
+// weights, consecutive column tiles share the gathered rows), which keeps the reuse
+// inside one L2.
 //
 // Tiles (BM x BN x BK): 256x256x32 with 8 waves (2x4, wave tile 128x64), 128x128 with
 // 4 waves, 32x128x64 with 2 waves; each wave's tile is built from
 // v_mfma_f32_32x32x16_bf16. LDS holds two stages of an A and a B tile, filled from two
-// register sets loaded two tiles ahead. Operands whose reduction index is contiguous in
-// memory are stored [rows][BK] with 16-byte chunks swizzled per row and read with 16-byte
-// LDS loads; operands contiguous
-// along M or N are stored as loaded, [BK][cols+16], and read with ds_read_b64_tr_b16
+// register sets loaded two tiles ahead; the eight-wave grouped-M kernels run the two
+// wave groups of each SIMD half a k-step apart (ping-pong), one multiplying while the
+// other reads fragments and stages the next tile. Operands whose reduction index is
+// contiguous in memory are stored [rows][BK] with 16-byte chunks swizzled per row and
+// read with 16-byte LDS loads; operands contiguous along M or N are stored as loaded,
+// [BK][cols+16], and read with ds_read_b64_tr_b16
 // (transposing LDS reads), so no operand is transposed in registers. The +16 padding is
 // the measured best for the transposing reads (94 B/clk per CU, against 83 with +32 and
 // 64 unpadded). Outputs are staged through LDS so every row leaves as whole 128-byte
