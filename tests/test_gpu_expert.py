@@ -79,7 +79,16 @@ def test_more_tiles_than_workgroups():
     workgroups at once, so each persistent workgroup walks several tiles (next-tile loads
     issued before an epilogue), each expert ending in a ragged tile."""
     d = synth.case(N=10000, H=256, I=256, E=8, K=8, seed=7, p_invalid=0.1)
-    run_case(d)
+    gi, _ = run_case(d)
+    # the concatenated W_up layout takes the same tile walk: bit-equal to the interleaved
+    # run wherever the concatenated-layout test requires it
+    gc = Gpu(d, layout=1)
+    gc.build()
+    gc.forward()
+    gc.backward()
+    for a, b in [(gi.out, gc.out), (gi.h, gc.h), (gi.dw_down, gc.dw_down), (gi.dtw, gc.dtw)]:
+        assert np.array_equal(np64(a), np64(b))
+    assert np.array_equal(gateup_to_concat(np64(gi.dw_up)), np64(gc.dw_up))
 
 
 def test_duplicate_experts_in_a_row_and_empty_rows():
