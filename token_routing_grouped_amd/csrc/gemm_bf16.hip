@@ -755,11 +755,16 @@ hipError_t launch_tiles(int bm, int bn, int bk, int grid, const GemmArgs &g, hip
     auto kern = gemm_bf16_kernel<MODE, A_KC, B_KC, EPI, BM_, BN_, BK_, WGM_, WGN_, GA>;    \
     int blocks = grid;                                                                    \
     if constexpr (MODE == GROUPED_M) {                                                    \
-      static int occ = 0; /* workgroups per CU, a property of the kernel */               \
-      if (occ == 0 &&                                                                     \
-          hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, 64 * WGM_ * WGN_, 0) != \
-              hipSuccess)                                                                 \
-        return hipErrorInvalidValue;                                                      \
+      /* workgroups per CU, a property of the kernel: queried once (a function-local     \
+         static is initialised once even when host threads race to the first launch) */   \
+      static const int occ = [&] {                                                        \
+        int o = 0;                                                                        \
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, 64 * WGM_ * WGN_, 0) == \
+                       hipSuccess                                                         \
+                   ? o                                                                    \
+                   : -1;                                                                  \
+      }();                                                                                \
+      if (occ < 0) return hipErrorInvalidValue;                                           \
       int dev = 0, ncu = 0;                                                               \
       if (hipGetDevice(&dev) != hipSuccess ||                                             \
           hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) !=      \
