@@ -19,6 +19,7 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -144,9 +145,15 @@ def cpu_baseline(d, backward: bool, target_s: float):
     t0 = time.perf_counter()
     oracle.build_metadata(idx, w, E)
     t_meta = time.perf_counter() - t0
+    cpu_model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next(l.split(":", 1)[1].strip() for l in fh if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return {
         "value": P * mult / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-        "kind": "oracle",
+        "kind": "oracle", "cpu_model": cpu_model,
         "sample": (f"first {n} of {idx.shape[0]} rows ({P} pairs): metadata + forward"
                    f"{' + backward' if backward else ''} in fp64, {t:.1f} s"),
         "metadata_us_full_workload": t_meta * 1e6,
@@ -257,8 +264,8 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one rank's local expert layer on one GPU; --gpus {args.gpus} "
-              f"(WORLD_SIZE={world}) is not supported in this build", file=sys.stderr)
+        print(f"bench.py measures one rank's local expert layer on one GPU: --gpus {args.gpus} "
+              f"(WORLD_SIZE={world}) is not supported", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -47,7 +47,7 @@ typedef enum {
   MOE_OK = 0,
   MOE_EINVAL = 1,       /* bad argument */
   MOE_ENOSPC = 2,       /* workspace smaller than the matching *_workspace() query */
-  MOE_EUNSUPPORTED = 3, /* shape/dtype/layout this build does not implement */
+  MOE_EUNSUPPORTED = 3, /* shape/dtype/layout this library does not implement */
   MOE_EHIP = 4          /* a HIP launch failed */
 } moe_status;
 
@@ -73,7 +73,7 @@ typedef enum { MOE_GATEUP_INTERLEAVED = 0, MOE_GATEUP_CONCAT = 1 } moe_gateup_la
 /* Device status bits, OR-ed into *meta->status (zeroed by moe_build_metadata). */
 enum { MOE_DEV_BAD_EXPERT = 1u, MOE_DEV_OVER_CAPACITY = 2u };
 
-/* Limits of this build (checked synchronously). */
+/* Limits of this library (checked synchronously). */
 enum { MOE_MAX_EXPERTS = 1024, MOE_MAX_TOPK = 64 };
 
 /* Routing metadata (GitHub issue #68, the list of arrays SonicMoE's grouped GEMM
