@@ -104,6 +104,8 @@ def route(logits, K: int, mode: int, renormalize: bool = False) -> dict:
     logits [N,E] as bf16 bits (uint16), fp32 or fp64."""
     lg, dt = _typed(logits)
     N, E = lg.shape
+    if not 1 <= K <= E:
+        raise ValueError(f"route needs 1 <= K <= E (K={K}, E={E})")
     idx = np.zeros((N, K), np.int32)
     w = np.zeros((N, K), np.float64)
     aux = np.zeros(1, np.float64)

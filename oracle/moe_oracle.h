@@ -146,7 +146,7 @@ void oracle_sample_dw_up_cols(int64_t H, int64_t I, int64_t E,
  *   aux = E * sum_e f_e * P_e,  f_e = (slots routed to e) / (N*K),
  *   P_e = (1/N) * sum_t softmax over all E of logits[t,:], at e.
  * logits [N,E] typed (ORACLE_BF16 / F32 / F64). Outputs topk_idx [N,K],
- * topk_weights [N,K] (fp64), *aux (0 when N = 0). */
+ * topk_weights [N,K] (fp64), *aux (0 when N = 0). Requires 1 <= K <= E. */
 void oracle_route(int64_t N, int64_t E, int64_t K, const void *logits, int logits_dt, int mode,
                   int renormalize, int32_t *topk_idx, double *topk_weights, double *aux);
 
