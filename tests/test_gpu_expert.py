@@ -168,15 +168,24 @@ def test_n_zero():
     assert np.all(np64(g.dw_up) == 0) and np.all(np64(g.dw_down) == 0)
 
 
+CONCAT_CASES = {
+    "tiles256": dict(N=600, H=384, I=256, E=5, K=4, seed=21, p_invalid=0.3),
+    # at most 16 rows per expert on average: the 32-row tiles of the up projection
+    # and of the dSwiGLU backward, in both gate/up orders
+    "rows32": dict(N=96, H=256, I=256, E=16, K=2, seed=22, p_invalid=0.1),
+}
+
+
+@pytest.mark.parametrize("shape", list(CONCAT_CASES))
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-def test_concat_gate_up_layout(dtype):
+def test_concat_gate_up_layout(dtype, shape):
     """W_up stored [gates | ups] (MOE_GATEUP_CONCAT): the same layer as the interleaved
     storage of the same weights (the Hysen Labs page on SonicMoE, gate/up formats).
     Against the oracle, with dW_up compared in the concatenated order; against the
     interleaved run, the up-projection tiles hold the same values, so the forward and
     every gradient except dx (whose 2I contraction runs in another order) match bit for bit."""
-    d = synth.case(N=600, H=384, I=256, E=5, K=4, seed=21, p_invalid=0.3)
-    print(f"concat layout case dtype={dtype}", flush=True)
+    d = synth.case(**CONCAT_CASES[shape])
+    print(f"concat layout case {shape} dtype={dtype}", flush=True)
     m, f, gr = oracle_full(d)
     gi = Gpu(d, dtype=dtype)
     gc = Gpu(d, dtype=dtype, layout=1)
