@@ -855,12 +855,13 @@ hipError_t launch_gemm_bf16(GemmKind kind, const GemmArgs &g, hipStream_t st) {
       return launch_tiles<GROUPED_M, true, true, EPI_STORE, 0>(bm, bn, bk, grid, g, st);
     case kWeightGrad:
       // the gathered operand is a compile-time choice: the row-index loads of the loop
-      // then carry no condition
-      if (g.a_rows && g.b_rows)
-        return launch_tiles<VARLEN_K, false, false, EPI_STORE, 3>(bm, bn, bk, grid, g, st);
-      if (g.a_rows) return launch_tiles<VARLEN_K, false, false, EPI_STORE, 1>(bm, bn, bk, grid, g, st);
-      if (g.b_rows) return launch_tiles<VARLEN_K, false, false, EPI_STORE, 2>(bm, bn, bk, grid, g, st);
-      return launch_tiles<VARLEN_K, false, false, EPI_STORE, 0>(bm, bn, bk, grid, g, st);
+      // then carry no condition. Each weight gradient gathers exactly one operand
+      // (x rows for dW_up, dout rows for dW_down); other combinations are not built.
+      if (g.a_rows && !g.b_rows)
+        return launch_tiles<VARLEN_K, false, false, EPI_STORE, 1>(bm, bn, bk, grid, g, st);
+      if (g.b_rows && !g.a_rows)
+        return launch_tiles<VARLEN_K, false, false, EPI_STORE, 2>(bm, bn, bk, grid, g, st);
+      return hipErrorInvalidValue;
     default:
       return hipErrorInvalidValue;
   }
