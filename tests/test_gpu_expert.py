@@ -91,6 +91,15 @@ def test_more_tiles_than_workgroups():
     assert np.array_equal(gateup_to_concat(np64(gi.dw_up)), np64(gc.dw_up))
 
 
+@pytest.mark.parametrize("N,K", [(2000, 8), (24000, 8), (400, 64)])
+def test_max_experts(N, K):
+    """E = 1024 local experts (the largest the library takes) and K up to 64: the tile
+    tables, the tile-to-expert search and the weight gradients' expert ordering at their
+    largest; about 14 rows per expert (32-row tiles), about 170 (256-row tiles), and 64
+    slots per token."""
+    run_case(synth.case(N=N, H=128, I=128, E=1024, K=K, seed=31, p_invalid=0.1))
+
+
 def test_duplicate_experts_in_a_row_and_empty_rows():
     rng = np.random.default_rng(5)
     idx = rng.integers(0, 3, size=(200, 4)).astype(np.int32)

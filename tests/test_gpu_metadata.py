@@ -53,7 +53,8 @@ def test_workloads(name):
 @pytest.mark.parametrize("seed", range(4))
 @pytest.mark.parametrize("N,K,E,p", [(1, 1, 1, 0.0), (3, 2, 3, 0.3), (1000, 8, 64, 0.5),
                                      (4097, 6, 17, 0.2), (2048, 1, 1, 0.1),
-                                     (3000, 16, 1024, 0.0), (50000, 3, 5, 0.9)])
+                                     (3000, 16, 1024, 0.0), (50000, 3, 5, 0.9),
+                                     (2000, 64, 1024, 0.2), (500, 64, 3, 0.0)])
 def test_random(N, K, E, p, seed):
     rng = np.random.default_rng(seed)
     idx = rng.integers(0, E, size=(N, K)).astype(np.int32)  # duplicates in a row allowed
