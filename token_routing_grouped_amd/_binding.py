@@ -108,6 +108,7 @@ class Metadata:
         self.num_activated_expert_per_token_offset = torch.empty(N + 1, **i32)
         self.router_scores = torch.empty(c, dtype=torch.float32, device=device)
         self.status = torch.empty(1, **i32)
+        self.device = self.status.device
         self._c = _CMeta(self.N, self.K, self.E, cap,
                          *[t.data_ptr() for t in (
                              self.expert_frequency, self.expert_frequency_offset,
@@ -142,6 +143,20 @@ def _dev(t: torch.Tensor, name: str, dtype=None, shape=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _dev_on(meta: "Metadata", t, name: str, dtype=None, shape=None):
+    """_dev, and the tensor must be on the metadata's device."""
+    if isinstance(t, torch.Tensor) and t.device != meta.device:
+        raise ValueError(f"{name} is on {t.device}, the metadata on {meta.device}")
+    return _dev(t, name, dtype, shape)
+
+
+def _on(meta: "Metadata", stream):
+    """The call runs with the metadata's device current; an explicit stream must be on it."""
+    if stream is not None and stream.device != meta.device:
+        raise ValueError(f"stream is on {stream.device}, the metadata on {meta.device}")
+    return torch.cuda.device(meta.device)
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return MOE_BF16
@@ -153,6 +168,8 @@ def _dtype_code(t: torch.Tensor) -> int:
 def _workspace(workspace, need: int, device, stream):
     """(tensor, pointer, bytes). A workspace allocated here is tied to the stream the
     call runs on; the caller keeps the tensor alive until after the call."""
+    if workspace is not None and workspace.device != torch.device(device):
+        raise ValueError(f"workspace is on {workspace.device}, the call on {device}")
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
         if stream is not None:
@@ -175,12 +192,13 @@ def moe_expert_backward_workspace(meta: Metadata, H: int, I: int, dtype: int = M
 
 def moe_build_metadata(topk_idx, topk_weights, meta: Metadata, workspace=None, stream=None):
     N, K = meta.N, meta.K
-    pi = _dev(topk_idx, "topk_idx", torch.int32, (N, K))
-    pw = _dev(topk_weights, "topk_weights", torch.float32, (N, K))
+    pi = _dev_on(meta, topk_idx, "topk_idx", torch.int32, (N, K))
+    pw = _dev_on(meta, topk_weights, "topk_weights", torch.float32, (N, K))
     need = moe_build_metadata_workspace(N, K, meta.E)
     wst, ws, nb = _workspace(workspace, need, topk_idx.device, stream)
-    _check(lib().moe_build_metadata(pi, pw, meta.ptr, ws, nb, _stream(stream)),
-           "moe_build_metadata")
+    with _on(meta, stream):
+        _check(lib().moe_build_metadata(pi, pw, meta.ptr, ws, nb, _stream(stream)),
+               "moe_build_metadata")
     return wst
 
 
@@ -196,20 +214,21 @@ def moe_route(logits, meta: Metadata, mode: int = MOE_ROUTE_SOFTMAX_TOPK, renorm
     None); output tensors may be passed in."""
     N, K, E = meta.N, meta.K, meta.E
     dev = logits.device
-    pl = _dev(logits, "logits", logits.dtype, (N, E))
+    pl = _dev_on(meta, logits, "logits", logits.dtype, (N, E))
     if topk_idx is None:
         topk_idx = torch.empty(N, K, dtype=torch.int32, device=dev)
     if topk_weights is None:
         topk_weights = torch.empty(N, K, dtype=torch.float32, device=dev)
     if aux_loss is None and want_aux:
         aux_loss = torch.empty(1, dtype=torch.float32, device=dev)
-    pi = _dev(topk_idx, "topk_idx", torch.int32, (N, K))
-    pw = _dev(topk_weights, "topk_weights", torch.float32, (N, K))
-    pa = None if aux_loss is None else _dev(aux_loss, "aux_loss", torch.float32, (1,))
+    pi = _dev_on(meta, topk_idx, "topk_idx", torch.int32, (N, K))
+    pw = _dev_on(meta, topk_weights, "topk_weights", torch.float32, (N, K))
+    pa = None if aux_loss is None else _dev_on(meta, aux_loss, "aux_loss", torch.float32, (1,))
     need = moe_route_workspace(N, K, E)
     wst, ws, nb = _workspace(workspace, need, dev, stream)
-    _check(lib().moe_route(pl, _dtype_code(logits), int(mode), int(bool(renormalize)), pi, pw,
-                           pa, meta.ptr, ws, nb, _stream(stream)), "moe_route")
+    with _on(meta, stream):
+        _check(lib().moe_route(pl, _dtype_code(logits), int(mode), int(bool(renormalize)), pi,
+                               pw, pa, meta.ptr, ws, nb, _stream(stream)), "moe_route")
     return topk_idx, topk_weights, aux_loss
 
 
@@ -219,15 +238,16 @@ def moe_expert_forward(meta: Metadata, x, w_up, w_down, out, h_save=None, worksp
     H = x.shape[1]
     I = w_down.shape[1]
     dt = _dtype_code(x)
-    px = _dev(x, "x", x.dtype, (N, H))
-    pu = _dev(w_up, "w_up", x.dtype, (E, H, 2 * I))
-    pd = _dev(w_down, "w_down", x.dtype, (E, I, H))
-    po = _dev(out, "out", x.dtype, (N, H))
-    ph = None if h_save is None else _dev(h_save, "h_save", x.dtype, (meta.capacity, 2 * I))
+    px = _dev_on(meta, x, "x", x.dtype, (N, H))
+    pu = _dev_on(meta, w_up, "w_up", x.dtype, (E, H, 2 * I))
+    pd = _dev_on(meta, w_down, "w_down", x.dtype, (E, I, H))
+    po = _dev_on(meta, out, "out", x.dtype, (N, H))
+    ph = None if h_save is None else _dev_on(meta, h_save, "h_save", x.dtype, (meta.capacity, 2 * I))
     need = moe_expert_forward_workspace(meta, H, I, dt)
     wst, ws, nb = _workspace(workspace, need, x.device, stream)
-    _check(lib().moe_expert_forward(meta.ptr, px, pu, pd, H, I, dt, layout, ph, po, ws, nb,
-                                    _stream(stream)), "moe_expert_forward")
+    with _on(meta, stream):
+        _check(lib().moe_expert_forward(meta.ptr, px, pu, pd, H, I, dt, layout, ph, po, ws, nb,
+                                        _stream(stream)), "moe_expert_forward")
 
 
 def moe_expert_backward(meta: Metadata, topk_idx, x, w_up, w_down, h_saved, dout, dx, dw_up,
@@ -238,23 +258,24 @@ def moe_expert_backward(meta: Metadata, topk_idx, x, w_up, w_down, h_saved, dout
     I = w_down.shape[1]
     dt = _dtype_code(x)
     args = [
-        _dev(topk_idx, "topk_idx", torch.int32, (N, K)),
-        _dev(x, "x", x.dtype, (N, H)),
-        _dev(w_up, "w_up", x.dtype, (E, H, 2 * I)),
-        _dev(w_down, "w_down", x.dtype, (E, I, H)),
-        _dev(h_saved, "h_saved", x.dtype, (meta.capacity, 2 * I)),
-        _dev(dout, "dout", x.dtype, (N, H)),
+        _dev_on(meta, topk_idx, "topk_idx", torch.int32, (N, K)),
+        _dev_on(meta, x, "x", x.dtype, (N, H)),
+        _dev_on(meta, w_up, "w_up", x.dtype, (E, H, 2 * I)),
+        _dev_on(meta, w_down, "w_down", x.dtype, (E, I, H)),
+        _dev_on(meta, h_saved, "h_saved", x.dtype, (meta.capacity, 2 * I)),
+        _dev_on(meta, dout, "dout", x.dtype, (N, H)),
     ]
     outs = [
-        _dev(dx, "dx", x.dtype, (N, H)),
-        _dev(dw_up, "dw_up", x.dtype, (E, H, 2 * I)),
-        _dev(dw_down, "dw_down", x.dtype, (E, I, H)),
-        _dev(d_topk_weights, "d_topk_weights", torch.float32, (N, K)),
+        _dev_on(meta, dx, "dx", x.dtype, (N, H)),
+        _dev_on(meta, dw_up, "dw_up", x.dtype, (E, H, 2 * I)),
+        _dev_on(meta, dw_down, "dw_down", x.dtype, (E, I, H)),
+        _dev_on(meta, d_topk_weights, "d_topk_weights", torch.float32, (N, K)),
     ]
     need = moe_expert_backward_workspace(meta, H, I, dt)
     wst, ws, nb = _workspace(workspace, need, x.device, stream)
-    _check(lib().moe_expert_backward(meta.ptr, *args, H, I, dt, layout, *outs, ws, nb,
-                                     _stream(stream)), "moe_expert_backward")
+    with _on(meta, stream):
+        _check(lib().moe_expert_backward(meta.ptr, *args, H, I, dt, layout, *outs, ws, nb,
+                                         _stream(stream)), "moe_expert_backward")
 
 
 def moe_kernel_name(kernel: int) -> str:
