@@ -101,10 +101,12 @@ def test_bad_expert_ids_set_status():
         assert np.array_equal(bad[k], got[k]), k
 
 
-@pytest.mark.parametrize("N,K,E", [(300000, 8, 64), (2200000, 1, 7), (140000, 16, 1024)])
+@pytest.mark.parametrize("N,K,E", [(300000, 8, 64), (2200000, 1, 7), (140000, 16, 1024),
+                                   (600000, 8, 64)])
 def test_long_columns_two_pass_scan(N, K, E):
-    """More than 2048 chunks (of 1024 slots at these sizes): the column scan runs in
-    segments (a pass of segment sums, then the segments with their bases)."""
+    """More than 2048 chunks (of 1024 slots at the first three sizes, of 2048 at the
+    last): the column scan runs in segments (a pass of segment sums, then the segments
+    with their bases)."""
     rng = np.random.default_rng(N + K + E)
     idx = rng.integers(0, E, size=(N, K)).astype(np.int32)
     idx[rng.random((N, K)) < 0.25] = -1
@@ -113,11 +115,12 @@ def test_long_columns_two_pass_scan(N, K, E):
 
 
 @pytest.mark.parametrize("NK", [(1 << 18) - 1, 1 << 18, (1 << 18) + 1,
-                                (1 << 20) - 1, 1 << 20, (1 << 20) + 1])
+                                (1 << 20) - 1, 1 << 20, (1 << 20) + 1,
+                                (1 << 22) - 1, 1 << 22, (1 << 22) + 1])
 def test_slot_count_thresholds(NK):
     """Either side of the slot counts where the scatter starts staging its sorted writes
-    in LDS (2^18) and where the chunks grow from 512 to 1024 slots (2^20); K = 1 so that
-    every slot count is reachable, with a ragged last chunk."""
+    in LDS (2^18) and where the chunks grow from 512 to 1024 slots (2^20) and to 2048
+    (2^22); K = 1 so that every slot count is reachable, with a ragged last chunk."""
     rng = np.random.default_rng(NK)
     E = 48
     idx = rng.integers(0, E, size=(NK, 1)).astype(np.int32)

@@ -110,16 +110,17 @@ def test_route_then_forward():
     assert_close(np64(out), f["out"], TOL["bf16"], "out")
 
 
-def test_route_long_columns():
-    """Over 2048 metadata chunks (of 1024 slots at this size): the counts and the aux
-    loss's probability columns are reduced in two passes."""
-    lg = synth.router_logits(300000, 64, seed=21)
+@pytest.mark.parametrize("N,E", [(300000, 64), (600000, 32)])
+def test_route_long_columns(N, E):
+    """Over 2048 metadata chunks (of 1024 slots at 2.4M slots, of 2048 at 4.8M): the
+    counts and the aux loss's probability columns are reduced in two passes."""
+    lg = synth.router_logits(N, E, seed=21)
     check(*run_route(lg, 8, 1, False))
 
 
-@pytest.mark.parametrize("N,K", [(32768, 8), (131072, 8), (262143, 4)])
+@pytest.mark.parametrize("N,K", [(32768, 8), (131072, 8), (262143, 4), (524288, 8)])
 def test_route_slot_count_thresholds(N, K):
     """Router at the slot counts where the metadata chunks and the scatter's write-out
-    change (2^18 and 2^20 slots), and a ragged last chunk."""
+    change (2^18, 2^20 and 2^22 slots), and a ragged last chunk."""
     lg = synth.router_logits(N, 32, seed=N + K)
     check(*run_route(lg, K, 1, True))

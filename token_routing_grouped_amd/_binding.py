@@ -5,6 +5,7 @@ loaded (same soname), and torch's streams and device pointers are valid for it.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -151,10 +152,13 @@ def _dev_on(meta: "Metadata", t, name: str, dtype=None, shape=None):
 
 
 def _on(meta: "Metadata", stream):
-    """The call runs with the metadata's device current; an explicit stream must be on it."""
+    """The call runs with the metadata's device current (switched only when another one
+    is); an explicit stream must be on it."""
     if stream is not None and stream.device != meta.device:
         raise ValueError(f"stream is on {stream.device}, the metadata on {meta.device}")
-    return torch.cuda.device(meta.device)
+    if torch.cuda.current_device() != meta.device.index:
+        return torch.cuda.device(meta.device)
+    return contextlib.nullcontext()
 
 
 def _dtype_code(t: torch.Tensor) -> int:

@@ -8,9 +8,12 @@ namespace moe {
 // ---- routing metadata -------------------------------------------------------
 constexpr int kMetaThreads = 256;
 // Slots per thread of the metadata kernels: 2 (chunks of 512 slots, enough workgroups
-// to fill the chip) below 2^20 slots, else 4 (chunks of 1024: longer runs per expert in
-// the sorted writes and fewer, shorter prefix columns; measured 84 -> 70 us at 2^23 slots).
-inline int meta_items(int64_t NK) { return NK >= ((int64_t)1 << 20) ? 4 : 2; }
+// to fill the chip) below 2^20 slots, 4 (chunks of 1024) below 2^22, else 8: longer runs
+// per expert in the sorted writes and fewer, shorter prefix columns as the slots grow
+// (512 -> 1024 measured 84 -> 70 us at 2^23 slots).
+inline int meta_items(int64_t NK) {
+  return NK >= ((int64_t)1 << 22) ? 8 : NK >= ((int64_t)1 << 20) ? 4 : 2;
+}
 inline int meta_chunk(int64_t NK) { return kMetaThreads * meta_items(NK); }
 
 struct MetaOut {

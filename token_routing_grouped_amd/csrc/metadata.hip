@@ -313,7 +313,10 @@ hipError_t launch_meta_hist(const int32_t *topk_idx, int N, int K, int E, int32_
   const int64_t NK = (int64_t)N * K;
   const MetaWs L = meta_ws_layout(NK, E);
   const size_t sh = (size_t)(E + 2) * sizeof(int32_t);
-  if (meta_items(NK) == 4)
+  if (meta_items(NK) == 8)
+    hipLaunchKernelGGL(meta_hist_kernel<8>, dim3(L.nblk), dim3(kMetaThreads), sh, stream, topk_idx,
+                       NK, E, ws + L.hist);
+  else if (meta_items(NK) == 4)
     hipLaunchKernelGGL(meta_hist_kernel<4>, dim3(L.nblk), dim3(kMetaThreads), sh, stream, topk_idx,
                        NK, E, ws + L.hist);
   else
@@ -349,7 +352,10 @@ hipError_t launch_meta_scatter(const int32_t *topk_idx, const float *topk_weight
   while ((1 << nbits) < E) nbits++;
   const size_t sh = (size_t)(2 * (E + 2) + 4 * E + 8 + (E + 1) + 3 * meta_chunk(NK) +
                              (out.aux ? E : 0)) * sizeof(int32_t);
-  if (meta_items(NK) == 4)
+  if (meta_items(NK) == 8)
+    hipLaunchKernelGGL(meta_scatter_kernel<8>, dim3(L.nblk), dim3(kMetaThreads), sh, stream,
+                       topk_idx, topk_weights, N, K, E, nbits, capacity, ws + L.pre, ws + L.tot, out);
+  else if (meta_items(NK) == 4)
     hipLaunchKernelGGL(meta_scatter_kernel<4>, dim3(L.nblk), dim3(kMetaThreads), sh, stream,
                        topk_idx, topk_weights, N, K, E, nbits, capacity, ws + L.pre, ws + L.tot, out);
   else
