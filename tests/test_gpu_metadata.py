@@ -102,7 +102,7 @@ def test_bad_expert_ids_set_status():
 
 
 @pytest.mark.parametrize("N,K,E", [(300000, 8, 64), (2200000, 1, 7), (140000, 16, 1024),
-                                   (600000, 8, 64)])
+                                   (600000, 8, 64), (300000, 16, 1024)])
 def test_long_columns_two_pass_scan(N, K, E):
     """More than 2048 chunks (of 1024 slots at the first three sizes, of 2048 at the
     last): the column scan runs in segments (a pass of segment sums, then the segments

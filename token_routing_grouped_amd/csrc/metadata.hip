@@ -150,18 +150,22 @@ __global__ __launch_bounds__(kMetaThreads) void meta_scan_kernel(
   if (tid == 0 && seg == nseg - 1) tot[c] = s_base + t;
 }
 
-template <int ITEMS>
-__global__ __launch_bounds__(kMetaThreads) void meta_scatter_kernel(
+// NW wavefronts per workgroup; each ranks ITEMS rounds of 64 slots of its share of the
+// chunk (the 2048-slot chunks take 8 wavefronts, so a wavefront's rounds stay at 4)
+template <int ITEMS, int NW>
+__global__ __launch_bounds__(64 * NW) void meta_scatter_kernel(
     const int32_t *__restrict__ idx, const float *__restrict__ wts, int N, int K, int E,
     int nbits, int cap, const int32_t *__restrict__ pre, const int32_t *__restrict__ tot,
     MetaOut out) {
-  constexpr int CHUNK = kMetaThreads * ITEMS;
+  constexpr int NT = 64 * NW;
+  constexpr int CHUNK = NT * ITEMS;
+  static_assert(NW <= 8, "per-wave valid counts");
   extern __shared__ int32_t sh[];
   int32_t *s_off = sh;              // [E+2]: totals, scanned in place -> offsets, [E] = P,
                                     // [E+1] = bad-id flags
   int32_t *s_base = s_off + E + 2;  // [E+2]: this chunk's prefix row -> bases
-  int32_t *s_run = s_base + E + 2;  // [4][E] per-wave running counts
-  int32_t *s_misc = s_run + 4 * E;  // [8]: per-wave valid counts
+  int32_t *s_run = s_base + E + 2;  // [NW][E] per-wave running counts
+  int32_t *s_misc = s_run + NW * E;  // [8]: per-wave valid counts
   int32_t *s_loc = s_misc + 8;      // [E+1]: this chunk's slots of experts < e (in-chunk)
   int32_t *s_ps = s_loc + E + 1;    // [CHUNK] sorted position of the k-th sorted slot
   int32_t *s_pt = s_ps + CHUNK;     // [CHUNK] its token
@@ -183,7 +187,7 @@ __global__ __launch_bounds__(kMetaThreads) void meta_scatter_kernel(
 
   // this wave's slots (the w-th quarter of the chunk, rounds of 64), the chunk's
   // prefix row and the totals: all loads issued together
-  const int64_t wbase = (int64_t)me * CHUNK + (int64_t)w * (CHUNK / 4);
+  const int64_t wbase = (int64_t)me * CHUNK + (int64_t)w * (CHUNK / NW);
   int r_e[ITEMS];
   float r_w[ITEMS];
 #pragma unroll
@@ -195,7 +199,7 @@ __global__ __launch_bounds__(kMetaThreads) void meta_scatter_kernel(
   const int32_t *prow = pre + (int64_t)me * W;
   const bool aux = me == 0 && out.aux;  // router: the load-balancing loss
   float *s_prod = (float *)(s_pq + CHUNK);  // [E] (router only)
-  for (int c = tid; c < W; c += kMetaThreads) {
+  for (int c = tid; c < W; c += NT) {
     s_base[c] = prow[c];
     if (c <= E) {
       const int t = tot[c];
@@ -204,7 +208,7 @@ __global__ __launch_bounds__(kMetaThreads) void meta_scatter_kernel(
       if (aux && c < E) s_prod[c] = out.psum ? (float)t * out.psum[c] : 0.0f;
     }
   }
-  for (int i = tid; i < 4 * E + 8; i += kMetaThreads) s_run[i] = 0;
+  for (int i = tid; i < NW * E + 8; i += NT) s_run[i] = 0;
   __syncthreads();
   if (aux && tid < kWave) {  // lane-strided partials, then the wave sum: fixed order
     float a = 0.0f;
@@ -216,7 +220,7 @@ __global__ __launch_bounds__(kMetaThreads) void meta_scatter_kernel(
   __syncthreads();
   const int P = s_off[E];
   if (me == 0) {
-    for (int e = tid; e <= E; e += kMetaThreads) out.expert_frequency_offset[e] = s_off[e];
+    for (int e = tid; e <= E; e += NT) out.expert_frequency_offset[e] = s_off[e];
     if (tid == 0) {
       out.tok_off[N] = P;
       uint32_t st = 0;
@@ -226,7 +230,7 @@ __global__ __launch_bounds__(kMetaThreads) void meta_scatter_kernel(
     }
   }
   const int valid_before = s_base[E + 1];
-  for (int e = tid; e < E; e += kMetaThreads) s_base[e] += s_off[e];  // base of this chunk
+  for (int e = tid; e < E; e += NT) s_base[e] += s_off[e];  // base of this chunk
 
   // ---- stable in-chunk ranks
   int r_rank[ITEMS], r_vrank[ITEMS];
@@ -260,8 +264,12 @@ __global__ __launch_bounds__(kMetaThreads) void meta_scatter_kernel(
   // slots); below, each lane writes its own slot's entries (0.5 us less at 2^17).
   const bool staged = NK >= ((int64_t)1 << 18);
   if (staged) {
-    for (int e = tid; e < E; e += kMetaThreads)
-      s_loc[e] = s_run[e] + s_run[E + e] + s_run[2 * E + e] + s_run[3 * E + e];
+    for (int e = tid; e < E; e += NT) {
+      int c = 0;
+#pragma unroll
+      for (int q = 0; q < NW; q++) c += s_run[q * E + e];
+      s_loc[e] = c;
+    }
     __syncthreads();
     wave0_exclusive_scan(s_loc, E);  // s_loc[e] = in-chunk slots of experts < e, [E] = total
     __syncthreads();
@@ -299,7 +307,7 @@ __global__ __launch_bounds__(kMetaThreads) void meta_scatter_kernel(
   if (!staged) return;
   __syncthreads();
   const int nloc = s_loc[E];
-  for (int pl = tid; pl < nloc; pl += kMetaThreads) {
+  for (int pl = tid; pl < nloc; pl += NT) {
     const int s = s_ps[pl];
     if ((unsigned)s < (unsigned)cap) {
       out.x_gather_idx[s] = s_pt[pl];
@@ -350,16 +358,24 @@ hipError_t launch_meta_scatter(const int32_t *topk_idx, const float *topk_weight
   const MetaWs L = meta_ws_layout(NK, E);
   int nbits = 0;
   while ((1 << nbits) < E) nbits++;
-  const size_t sh = (size_t)(2 * (E + 2) + 4 * E + 8 + (E + 1) + 3 * meta_chunk(NK) +
+  const int items = meta_items(NK);
+  const int nw = items == 8 ? 8 : 4;  // wavefronts of the scatter workgroup
+  const size_t sh = (size_t)(2 * (E + 2) + nw * E + 8 + (E + 1) + 3 * meta_chunk(NK) +
                              (out.aux ? E : 0)) * sizeof(int32_t);
-  if (meta_items(NK) == 8)
-    hipLaunchKernelGGL(meta_scatter_kernel<8>, dim3(L.nblk), dim3(kMetaThreads), sh, stream,
+  if (items == 8) {
+    // with 1024 experts the eight waves' running counts take the stage past the 64 KB of
+    // dynamic LDS a launch gets by default (a workgroup may use up to 160 KB); set once
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&meta_scatter_kernel<4, 8>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((meta_scatter_kernel<4, 8>), dim3(L.nblk), dim3(64 * 8), sh, stream,
                        topk_idx, topk_weights, N, K, E, nbits, capacity, ws + L.pre, ws + L.tot, out);
-  else if (meta_items(NK) == 4)
-    hipLaunchKernelGGL(meta_scatter_kernel<4>, dim3(L.nblk), dim3(kMetaThreads), sh, stream,
+  } else if (items == 4)
+    hipLaunchKernelGGL((meta_scatter_kernel<4, 4>), dim3(L.nblk), dim3(64 * 4), sh, stream,
                        topk_idx, topk_weights, N, K, E, nbits, capacity, ws + L.pre, ws + L.tot, out);
   else
-    hipLaunchKernelGGL(meta_scatter_kernel<2>, dim3(L.nblk), dim3(kMetaThreads), sh, stream,
+    hipLaunchKernelGGL((meta_scatter_kernel<2, 4>), dim3(L.nblk), dim3(64 * 4), sh, stream,
                        topk_idx, topk_weights, N, K, E, nbits, capacity, ws + L.pre, ws + L.tot, out);
   return hipGetLastError();
 }
