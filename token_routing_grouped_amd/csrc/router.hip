@@ -151,8 +151,9 @@ __device__ __forceinline__ float wave_sum_f32(float v) { return group_sum_f32<64
 
 // LPT lanes per token (8: E <= 128 and K <= 8; 16: E <= 256 and K <= 16; else 64), NV
 // logits per lane. Lane s of a token's group holds experts s, s+LPT, ...; after the
-// selection, lane k of the group holds the k-th expert.
-template <typename T, int LPT, int NV>
+// selection, lane k of the group holds the k-th expert. FULL: E == LPT * NV, so every
+// lane's NV experts exist and no per-logit bound is tested.
+template <typename T, int LPT, int NV, bool FULL>
 __global__ __launch_bounds__(kRouteThreads) void route_hist_kernel(
     const T *__restrict__ logits, int N, int E, int K, int mode, int renorm, int want_p,
     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, int32_t *__restrict__ hist,
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_hist_kernel(
 #pragma unroll
     for (int i = 0; i < NV; i++) {
       const int e = sl + LPT * i;
-      v[i] = e < E ? to_f32(logits[(int64_t)t * E + e]) : -INFINITY;
+      v[i] = (FULL || e < E) ? to_f32(logits[(int64_t)t * E + e]) : -INFINITY;
     }
     float lmax = -INFINITY;
 #pragma unroll
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_hist_kernel(
     float zl = 0.0f;
 #pragma unroll
     for (int i = 0; i < NV; i++) {
-      ex[i] = sl + LPT * i < E ? expf(v[i] - mx) : 0.0f;
+      ex[i] = (FULL || sl + LPT * i < E) ? expf(v[i] - mx) : 0.0f;
       zl += ex[i];
     }
     const float z_all = group_sum_f32<LPT>(zl);
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_hist_kernel(
 #pragma unroll
     for (int i = 0; i < NV; i++) {
       const uint32_t o = ordered(v[i]);
-      key[i] = sl + LPT * i < E ? (o > 1u ? o : 1u) : 0u;
+      key[i] = (FULL || sl + LPT * i < E) ? (o > 1u ? o : 1u) : 0u;
     }
     int my_e = 0;
     float my_v = 0.0f;
@@ -267,7 +268,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_hist_kernel(
 #pragma unroll
       for (int i = 0; i < NV; i++) {
         const int e = sl + LPT * i;
-        if (e < E) s_p[w * E + e] = pacc[i];
+        if (FULL || e < E) s_p[w * E + e] = pacc[i];
       }
     }
   }
@@ -299,9 +300,14 @@ hipError_t launch_route_hist(const void *logits, bool bf16, int N, int E, int K,
   const int need = (E + lpt - 1) / lpt;  // logits per lane, rounded up to a power of two
   const int nv = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 16;
 #define MOE_ROUTE(T, LPT, NV)                                                              \
-  hipLaunchKernelGGL((route_hist_kernel<T, LPT, NV>), dim3(L.nblk), dim3(kRouteThreads), sh, \
-                     stream, (const T *)logits, N, E, K, mode, renorm, (int)want_p, topk_idx, \
-                     topk_w, meta_ws + L.hist, ppart, meta_chunk((int64_t)N * K))
+  if (E == (LPT) * (NV))                                                                   \
+    hipLaunchKernelGGL((route_hist_kernel<T, LPT, NV, true>), dim3(L.nblk), dim3(kRouteThreads), \
+                       sh, stream, (const T *)logits, N, E, K, mode, renorm, (int)want_p,   \
+                       topk_idx, topk_w, meta_ws + L.hist, ppart, meta_chunk((int64_t)N * K)); \
+  else                                                                                     \
+    hipLaunchKernelGGL((route_hist_kernel<T, LPT, NV, false>), dim3(L.nblk), dim3(kRouteThreads), \
+                       sh, stream, (const T *)logits, N, E, K, mode, renorm, (int)want_p,   \
+                       topk_idx, topk_w, meta_ws + L.hist, ppart, meta_chunk((int64_t)N * K))
 #define MOE_ROUTE_NV(T, LPT)                                                               \
   switch (nv) {                                                                            \
     case 1: MOE_ROUTE(T, LPT, 1); break;                                                   \
