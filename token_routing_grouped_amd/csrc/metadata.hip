@@ -241,12 +241,17 @@ __global__ __launch_bounds__(64 * NW) void meta_scatter_kernel(
     const int e = r_e[it];
     const bool v = (unsigned)e < (unsigned)E;
     const uint64_t vm = ballot64(v);
-    // lanes of this round holding the same expert: agree with e on every id bit
+    // lanes of this round holding the same expert: agree with e on every id bit. Invalid
+    // lanes (e = -1) enter the ballots too but are not in vm, so never in m. Per bit:
+    // m &= bit ? bm : ~bm, as bm ^ (bit - 1) on each 32-bit half (bit - 1 is 0 or all ones)
     uint64_t m = vm;
     for (int b = 0; b < nbits; b++) {
-      const uint64_t bm = ballot64(v && ((e >> b) & 1));
-      const uint64_t S = (uint64_t)(int64_t)(-((e >> b) & 1));  // all ones where the bit is set
-      m &= S ^ ~bm;                                               // bit set: bm, else ~bm
+      const uint32_t bit = ((uint32_t)e >> b) & 1u;
+      const uint64_t bm = ballot64(bit != 0u);
+      const uint32_t t = bit - 1u;
+      const uint32_t lo = (uint32_t)m & ((uint32_t)bm ^ t);
+      const uint32_t hi = (uint32_t)(m >> 32) & ((uint32_t)(bm >> 32) ^ t);
+      m = ((uint64_t)hi << 32) | lo;
     }
     int prev = 0;
     if (v) prev = run[e];
