@@ -1,11 +1,16 @@
 """GPU path at the full workload sizes, in the configuration the benchmark times.
 
-The oracle cannot run these sizes in full, so it computes sampled outputs one
-by one (whole rows of out, dx, d_topk_weights for sampled tokens; rows of h;
-rows of dW_down and column pairs of dW_up for sampled experts, including the
-largest and an empty one), and properties that hold at any size are checked on
-the full tensors: metadata bit-exact, exact zeros for empty rows and experts,
-zeros of d_topk_weights at -1 slots.
+The oracle cannot run these sizes in full, so it computes sampled outputs one by
+one, drawn in strata so that every tile the GPU schedules is checked at least once:
+ - h: one row per (expert, 256-row tile) of the sorted positions (every row when the
+   layer is small);
+ - out, dx, d_topk_weights: the token of one sorted position per 256 (every token of a
+   small layer), plus the first, last and busiest token;
+ - dW_down: one row per (expert, 256-row tile of I); a row spans every column tile;
+ - dW_up: one (gate, up) column pair per (expert, 256-column tile of 2I); a column
+   spans every row tile.
+Properties that hold at any size are checked on the full tensors: metadata bit-exact,
+exact zeros for empty rows and experts, zeros of d_topk_weights at -1 slots.
 """
 import numpy as np
 import pytest
@@ -18,6 +23,36 @@ pytestmark = pytest.mark.gpu
 
 KEYS = ["expert_frequency", "expert_frequency_offset", "x_gather_idx", "s_scatter_idx",
         "s_reverse_scatter_idx", "num_activated_expert_per_token_offset", "router_scores"]
+TILE = 256  # stratum: the row and column tile of the grouped GEMMs at these sizes
+
+
+def strata(m, rng, N, I, idx):
+    """Sampled rows, tokens, dW_down rows and dW_up column pairs (see module docstring)."""
+    P, E = m["P"], m["E"]
+    foff, freq = m["expert_frequency_offset"], m["expert_frequency"]
+    h_rows = []
+    for e in range(E):
+        for r0 in range(int(foff[e]), int(foff[e + 1]), TILE):
+            h_rows.append(int(rng.integers(r0, min(r0 + TILE, int(foff[e + 1])))))
+    if P <= 4 * TILE:
+        h_rows = list(range(P))
+    valid_rows = (idx >= 0).sum(axis=1)
+    if N <= 4 * TILE:
+        toks = list(range(N))
+    else:
+        toks = [int(m["x_gather_idx"][int(rng.integers(s, min(s + TILE, P)))])
+                for s in range(0, P, TILE)]
+        toks += [0, N - 1, int(np.argmax(valid_rows))]
+    toks = np.array(sorted(set(toks)), np.int64)
+    dwd_e, dwd_j, dwu_e, dwu_j = [], [], [], []
+    for e in np.nonzero(freq)[0]:
+        for r0 in range(0, I, TILE):
+            dwd_e.append(int(e))
+            dwd_j.append(int(rng.integers(r0, min(r0 + TILE, I))))
+        for c0 in range(0, I, TILE // 2):  # pairs (2j, 2j+1): 128 pairs per column tile
+            dwu_e.append(int(e))
+            dwu_j.append(int(rng.integers(c0, min(c0 + TILE // 2, I))))
+    return h_rows, toks, (np.array(dwd_e), np.array(dwd_j)), (np.array(dwu_e), np.array(dwu_j))
 
 
 @pytest.mark.parametrize("name", ["qwen3_rank", "dsv3_rank", "decode", "long_prefill"])
@@ -45,23 +80,17 @@ def test_workload(name):
         assert np.array_equal(got[k], m[k].astype(got[k].dtype)), k
 
     rng = np.random.default_rng(1)
-    valid_rows = ((idx >= 0).sum(axis=1))
-    toks = sorted(set([0, N - 1, int(np.argmax(valid_rows))] +
-                      rng.choice(N, size=min(N, 9), replace=False).tolist()))
-    toks = np.array(toks, np.int64)
+    h_rows, toks, (dwd_e, dwd_j), (dwu_e, dwu_j) = strata(m, rng, N, I, idx)
+    print(f"workload {name}: {len(h_rows)} h rows, {len(toks)} tokens, {len(dwd_e)} dW_down "
+          f"rows, {len(dwu_e)} dW_up column pairs", flush=True)
+    hs = oracle.sample_h_rows(d["x"], d["w_up"], m, h_rows)
+    assert_close(np64(g.h[h_rows]), hs, tol, "h rows")
     st = oracle.sample_tokens(d["x"], d["w_up"], d["w_down"], idx, w, toks,
                               dout=d.get("dout") if cfg["backward"] else None)
     out = np64(g.out)
+    valid_rows = (idx >= 0).sum(axis=1)
     assert_close(out[toks], st["out"], tol, "out rows")
     assert np.all(out[valid_rows == 0] == 0)
-
-    freq = m["expert_frequency"]
-    foff = m["expert_frequency_offset"]
-    big = int(np.argmax(freq))
-    rows = sorted(set([0, int(foff[big]), int(foff[big + 1]) - 1, m["P"] - 1] +
-                      rng.choice(m["P"], size=4, replace=False).tolist()))
-    hs = oracle.sample_h_rows(d["x"], d["w_up"], m, rows)
-    assert_close(np64(g.h[rows]), hs, tol, "h rows")
 
     if not cfg["backward"]:
         return
@@ -71,18 +100,17 @@ def test_workload(name):
     assert np.all(dtw[idx < 0] == 0)
     assert np.all(np64(g.dx)[valid_rows == 0] == 0)
 
-    nz = np.nonzero(freq)[0]
-    small = int(nz[np.argmin(freq[nz])])
-    experts = sorted(set([big, small, int(rng.choice(nz))]))
-    el = np.repeat(experts, 2)
-    jl = rng.integers(0, I, size=el.shape[0])
-    dwd = oracle.sample_dw_down_rows(d["x"], d["w_up"], d["dout"], m, el, jl)
-    got_dwd = np.stack([np64(g.dw_down[int(e), int(j)]) for e, j in zip(el, jl)])
+    dwd = oracle.sample_dw_down_rows(d["x"], d["w_up"], d["dout"], m, dwd_e, dwd_j)
+    dw_down = g.dw_down
+    got_dwd = np64(dw_down[g.torch.from_numpy(dwd_e).to(dw_down.device),
+                           g.torch.from_numpy(dwd_j).to(dw_down.device)])
     assert_close(got_dwd, dwd, tol, "dw_down rows")
-    cols = oracle.sample_dw_up_cols(d["x"], d["w_up"], d["w_down"], d["dout"], m, el, jl)
-    got_cols = np.stack([np.stack([np64(g.dw_up[int(e), :, 2 * int(j)]),
-                                   np64(g.dw_up[int(e), :, 2 * int(j) + 1])])
-                         for e, j in zip(el, jl)])
+    cols = oracle.sample_dw_up_cols(d["x"], d["w_up"], d["w_down"], d["dout"], m, dwu_e, dwu_j)
+    dw_up = g.dw_up
+    te = g.torch.from_numpy(dwu_e).to(dw_up.device)
+    tj = g.torch.from_numpy(2 * dwu_j).to(dw_up.device)
+    got_cols = np.stack([np64(dw_up[te, :, tj]), np64(dw_up[te, :, tj + 1])], axis=1)
     assert_close(got_cols, cols, tol, "dw_up columns")
+    freq = m["expert_frequency"]
     for e in np.nonzero(freq == 0)[0]:
         assert np.all(np64(g.dw_up[int(e)]) == 0) and np.all(np64(g.dw_down[int(e)]) == 0)
