@@ -10,10 +10,13 @@ local experts, K=8 (the Qwen3.6 serving-script notes: 256 experts x top-8 at
 16384 tokens; GitHub issue #68: EP8 with DeepEP non-expand inputs).
 
 Prints one JSON line: throughput in TFLOP/s over valid pairs (18*P*H*I per
-forward+backward step), the routing-metadata build time and its fraction of
-HBM bandwidth, the dominant kernel against its roofline (timed with HIP events
-on its own stream through the library's kernel-timing hook), and the CPU oracle
-timed on a bounded sample of the same workload on this host.
+forward+backward step; the median of per-step event times after 10 warm-up steps),
+the routing-metadata build time and its fraction of HBM bandwidth, the dominant
+kernel against its roofline (timed with HIP events on its own stream through the
+library's kernel-timing hook), the CPU oracle timed on a bounded sample of the same
+workload on this host, and under "workloads" a few steps of each other benchmarked
+layer: the DeepSeek-V3-style and long-prefill rank shares (fwd+bwd) and decode
+(forward, weight-streaming GB/s).
 """
 import argparse
 import hashlib
@@ -95,6 +98,12 @@ class TimingEvent:
         if rc != 0:
             raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
         self.cuda_event = h.value
+
+    def record(self, stream_ptr: int) -> None:
+        rc = TimingEvent._hip.hipEventRecord(self._ct.c_void_p(self.cuda_event),
+                                             self._ct.c_void_p(stream_ptr))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
 
     def elapsed_time(self, end) -> float:
         ms = self._ct.c_float(0.0)
@@ -244,14 +253,210 @@ def router_timing(moe, synth, torch, np, N=32768, E=128, K=8, reps=20):
             "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
 
 
+def step_bytes_decode(d, P, active):
+    """Algorithmic HBM bytes of one forward (bf16): the active experts' weights, the
+    gathered x rows, h and a written, a re-read, y written and re-read, out written."""
+    N, H, I = d["N"], d["H"], d["I"]
+    return (active * 6 * H * I + 2 * P * H + 2 * P * 2 * I + 2 * 2 * P * I + 2 * 2 * P * H
+            + 2 * N * H)
+
+
+def measure(moe, synth, torch, np, name, seed, steps, warmup, cold_reps, stream):
+    """Times one workload: warm-up steps, the per-kernel durations (to name the dominant
+    kernel), then `steps` steps between a synchronisation on each side with an event
+    after every step (median and mean per step) and the dominant kernel bracketed by
+    events on its stream, then single cold steps. Returns (result dict, inputs)."""
+    cfg = synth.CONFIGS[name]
+    backward = cfg["backward"]
+    d = synth.make_inputs(name, seed, dout=backward)
+    N, H, I, E, K = d["N"], d["H"], d["I"], d["E"], d["K"]
+    P = int((d["topk_idx"] >= 0).sum())
+    dev = torch.device("cuda:0")
+
+    def t(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x, w_up, w_down = t(d["x"]), t(d["w_up"]), t(d["w_down"])
+    dout = t(d["dout"]) if backward else None
+    idx = torch.from_numpy(d["topk_idx"]).to(dev)
+    w = torch.from_numpy(d["topk_weights"]).to(dev)
+    # capacity = P, known on the host as DeepEP's handle knows total_pairs
+    meta = moe.Metadata(N, K, E, P, device=dev)
+    u8 = dict(dtype=torch.uint8, device=dev)
+    ws_meta = torch.empty(max(1, moe.moe_build_metadata_workspace(N, K, E)), **u8)
+    ws_fwd = torch.empty(max(1, moe.moe_expert_forward_workspace(meta, H, I)), **u8)
+    ws_bwd = (torch.empty(max(1, moe.moe_expert_backward_workspace(meta, H, I)), **u8)
+              if backward else None)
+    out = torch.empty(N, H, dtype=torch.bfloat16, device=dev)
+    h_save = torch.empty(P, 2 * I, dtype=torch.bfloat16, device=dev) if backward else None
+    if backward:
+        dx = torch.empty_like(x)
+        dw_up = torch.empty_like(w_up)
+        dw_down = torch.empty_like(w_down)
+        dtw = torch.empty(N, K, dtype=torch.float32, device=dev)
+
+    def build():
+        moe.moe_build_metadata(idx, w, meta, workspace=ws_meta)
+
+    def step():
+        build()
+        moe.moe_expert_forward(meta, x, w_up, w_down, out, h_save=h_save, workspace=ws_fwd)
+        if backward:
+            moe.moe_expert_backward(meta, idx, x, w_up, w_down, h_save, dout, dx, dw_up,
+                                    dw_down, dtw, workspace=ws_bwd)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    status = int(meta.status.item())
+    assert status == 0, f"device status {status}"
+    assert torch.isfinite(out.float()).all()
+
+    # per-kernel durations (3 launches each) to name the dominant kernel
+    # the kernels one step launches (the router is timed on its own)
+    step_kernels = [k for k in moe.KERNELS if not k.startswith("route")]
+    kernels = step_kernels if backward else step_kernels[:step_kernels.index("combine") + 1]
+    kernel_us = {}
+    for k in kernels:
+        ev = [TimingEvent() for _ in range(6)]
+        moe.moe_time_kernel(k, ev)
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        if moe.moe_time_kernel(k, None) < 3:
+            continue  # not launched at this size
+        kernel_us[k] = 1e3 * sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(3)) / 3
+    gemms = {k: v for k, v in kernel_us.items() if k in GEMM_FLOPS}
+    dominant = max(gemms, key=gemms.get)
+
+    # timed region: `steps` steps, an event after each, the dominant kernel bracketed
+    ev = [TimingEvent() for _ in range(2 * steps)]
+    marks = [TimingEvent() for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    moe.moe_time_kernel(dominant, ev)
+    wall0 = time.perf_counter()
+    stream_ptr = stream.cuda_stream
+    marks[0].record(stream_ptr)
+    for i in range(steps):
+        step()
+        marks[i + 1].record(stream_ptr)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    nrec = moe.moe_time_kernel(dominant, None)
+    assert nrec == steps, nrec
+    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
+    ms_med = per_step[len(per_step) // 2] if steps % 2 else \
+        0.5 * (per_step[steps // 2 - 1] + per_step[steps // 2])
+    ms_mean = marks[0].elapsed_time(marks[steps]) / steps
+    dom_times = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps))
+    dom_ms = sum(dom_times) / steps
+    assert int(meta.status.item()) == 0
+
+    # cold: each single step follows a 1 GiB fill that evicts L2 and the 256 MB MALL
+    cold = []
+    if cold_reps > 0:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        for _ in range(cold_reps):
+            flush.zero_()
+            marks[0].record(stream_ptr)
+            step()
+            marks[1].record(stream_ptr)
+            torch.cuda.synchronize()
+            cold.append(marks[0].elapsed_time(marks[1]))
+        del flush
+        cold.sort()
+
+    flops_step = (18 if backward else 6) * P * H * I
+    tflops = flops_step / (ms_med * 1e-3) / 1e12
+    dom_flops = GEMM_FLOPS[dominant] * P * H * I
+    dom_tflops = dom_flops / (dom_ms * 1e-3) / 1e12
+    active = int((np.bincount(d["topk_idx"][d["topk_idx"] >= 0].ravel(), minlength=E) > 0).sum())
+    dom_bytes = gemm_bytes(dominant, N, H, I, P, active)
+    # the roofline that bounds the kernel: HBM below the ridge intensity (decode), else MFMA
+    hbm_bound = dom_flops / dom_bytes < RIDGE
+    if hbm_bound:
+        roof = {"kernel": dominant, "bound": "hbm",
+                "achieved": round(dom_bytes / (dom_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": round(dom_bytes / (dom_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+    else:
+        roof = {"kernel": dominant, "bound": "mfma", "achieved": round(dom_tflops, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4)}
+    roof.update({"traffic": counted_traffic(dominant, name), "avg_us": round(dom_ms * 1e3, 2),
+                 "median_us": round(dom_times[len(dom_times) // 2] * 1e3, 2),
+                 "flops_per_launch": dom_flops, "bytes_per_launch": dom_bytes,
+                 "intensity_flop_per_byte": round(dom_flops / dom_bytes, 1)})
+    res = {
+        "N": N, "H": H, "I": I, "E": E, "K": K, "P": P, "seed": d["seed"],
+        "step": "metadata + forward" + (" + backward" if backward else ""),
+        "flops_per_step": flops_step, "ms_per_step": round(ms_med, 4),
+        "mean_ms_per_step": round(ms_mean, 4), "TFLOPs": round(tflops, 2),
+        "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "cold": ({"ms_per_step": round(cold[len(cold) // 2], 4),
+                  "TFLOPs": round(flops_step / (cold[len(cold) // 2] * 1e-3) / 1e12, 2),
+                  "reps": len(cold)} if cold else None),
+        "kernels_us": {k: round(v, 1) for k, v in kernel_us.items()},
+        "roofline": roof, "wall_s_timed": round(wall, 4), "steps": steps, "warmup": warmup,
+    }
+    if not backward:  # a forward at decode size streams the active experts' weights
+        nb = step_bytes_decode(d, P, active)
+        res.update({"us_per_step": round(ms_med * 1e3, 2), "active_experts": active,
+                    "bytes_per_step": nb,
+                    "GBps": round(nb / (ms_med * 1e-3) / 1e9, 1),
+                    "hbm_frac": round(nb / (ms_med * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)})
+    res["_handles"] = (idx, w, meta, ws_meta)
+    return res, d
+
+
+def metadata_alone(torch, moe, handles, stream, nm=50):
+    """Metadata build alone: device time of nm builds captured in one HIP graph (the
+    build never syncs with the host, so it captures) and replayed between events; and
+    the same nm calls issued from Python (bounded by host launch overhead)."""
+    idx, w, meta, ws_meta = handles
+
+    def build():
+        moe.moe_build_metadata(idx, w, meta, workspace=ws_meta)
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cap_stream = torch.cuda.Stream()
+    cap_stream.wait_stream(stream)
+    with torch.cuda.stream(cap_stream):
+        build()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap_stream):
+        for _ in range(nm):
+            build()
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = []
+    for _ in range(5):
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        reps.append(1e3 * e0.elapsed_time(e1) / nm)
+    reps.sort()
+    e0.record(stream)
+    for _ in range(nm):
+        build()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return reps[len(reps) // 2], 1e3 * e0.elapsed_time(e1) / nm
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3_rank")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="time only --workload (by default the line also carries a few steps "
+                         "of each other benchmarked workload)")
+    ap.add_argument("--other-steps", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--cold-reps", type=int, default=5,
                     help="single steps timed after a 1 GiB fill evicts L2 and the MALL")
@@ -287,183 +492,62 @@ def main():
         metadata_sweep(moe, synth, torch, np)
         return
 
-    cfg = synth.CONFIGS[args.workload]
-    backward = cfg["backward"]
-    d = synth.make_inputs(args.workload, args.seed, dout=backward)
-    N, H, I, E, K = d["N"], d["H"], d["I"], d["E"], d["K"]
-    P = int((d["topk_idx"] >= 0).sum())
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
-
-    def t(bits):
-        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
-
-    x, w_up, w_down = t(d["x"]), t(d["w_up"]), t(d["w_down"])
-    dout = t(d["dout"]) if backward else None
-    idx = torch.from_numpy(d["topk_idx"]).to(dev)
-    w = torch.from_numpy(d["topk_weights"]).to(dev)
-    # capacity = P, known on the host as DeepEP's handle knows total_pairs
-    meta = moe.Metadata(N, K, E, P, device=dev)
-    u8 = dict(dtype=torch.uint8, device=dev)
-    ws_meta = torch.empty(max(1, moe.moe_build_metadata_workspace(N, K, E)), **u8)
-    ws_fwd = torch.empty(max(1, moe.moe_expert_forward_workspace(meta, H, I)), **u8)
-    ws_bwd = torch.empty(max(1, moe.moe_expert_backward_workspace(meta, H, I)), **u8)
-    out = torch.empty(N, H, dtype=torch.bfloat16, device=dev)
-    h_save = torch.empty(P, 2 * I, dtype=torch.bfloat16, device=dev) if backward else None
-    if backward:
-        dx = torch.empty_like(x)
-        dw_up = torch.empty_like(w_up)
-        dw_down = torch.empty_like(w_down)
-        dtw = torch.empty(N, K, dtype=torch.float32, device=dev)
-
-    def build():
-        moe.moe_build_metadata(idx, w, meta, workspace=ws_meta)
-
-    def step():
-        build()
-        moe.moe_expert_forward(meta, x, w_up, w_down, out, h_save=h_save, workspace=ws_fwd)
-        if backward:
-            moe.moe_expert_backward(meta, idx, x, w_up, w_down, h_save, dout, dx, dw_up,
-                                    dw_down, dtw, workspace=ws_bwd)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    status = int(meta.status.item())
-    assert status == 0, f"device status {status}"
-    assert torch.isfinite(out.float()).all()
-
-    # per-kernel durations (3 launches each) to name the dominant kernel
-    # the kernels one step launches (the router is timed on its own below)
-    step_kernels = [k for k in moe.KERNELS if not k.startswith("route")]
-    kernels = step_kernels if backward else step_kernels[:step_kernels.index("combine") + 1]
-    kernel_us = {}
-    for k in kernels:
-        ev = [TimingEvent() for _ in range(6)]
-        moe.moe_time_kernel(k, ev)
-        for _ in range(3):
-            step()
-        torch.cuda.synchronize()
-        if moe.moe_time_kernel(k, None) < 3:
-            continue  # not launched at this size (meta_scan when the scan is folded)
-        kernel_us[k] = 1e3 * sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(3)) / 3
-    gemms = {k: v for k, v in kernel_us.items() if k in GEMM_FLOPS}
-    dominant = max(gemms, key=gemms.get)
-
-    # metadata build alone. Device time: nm builds captured in one HIP graph (the
-    # build never syncs with the host, so it captures) and replayed between events.
-    # Eager time: the same nm calls issued from Python, which bounds it by host
-    # launch overhead at these sizes.
-    nm = 50
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    cap_stream = torch.cuda.Stream()
-    cap_stream.wait_stream(stream)
-    with torch.cuda.stream(cap_stream):
-        build()
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=cap_stream):
-        for _ in range(nm):
-            build()
-    graph.replay()
-    torch.cuda.synchronize()
-    e0.record(stream)
-    graph.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    meta_us = 1e3 * e0.elapsed_time(e1) / nm
-    e0.record(stream)
-    for _ in range(nm):
-        build()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    meta_eager_us = 1e3 * e0.elapsed_time(e1) / nm
+    r, d = measure(moe, synth, torch, np, args.workload, args.seed, args.steps, args.warmup,
+                   args.cold_reps, stream)
+    meta_us, meta_eager_us = metadata_alone(torch, moe, r.pop("_handles"), stream)
+    N, E, K, P = r["N"], r["E"], r["K"], r["P"]
     meta_bytes = 8 * N * K + 16 * P + 4 * (N + 1) + 4 * E + 4 * (E + 1)
-
-    # timed region: K steps, the dominant kernel bracketed on its stream
-    ev = [TimingEvent() for _ in range(2 * args.steps)]
-    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    moe.moe_time_kernel(dominant, ev)
-    wall0 = time.perf_counter()
-    s0.record(stream)
-    for _ in range(args.steps):
-        step()
-    s1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    nrec = moe.moe_time_kernel(dominant, None)
-    assert nrec == args.steps, nrec
-    ms = s0.elapsed_time(s1) / args.steps
-    dom_ms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)) / args.steps
-    assert int(meta.status.item()) == 0
-
-    # cold: each single step follows a 1 GiB fill that evicts L2 and the 256 MB MALL
-    cold = []
-    if args.cold_reps > 0:
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        for _ in range(args.cold_reps):
-            flush.zero_()
-            s0.record(stream)
-            step()
-            s1.record(stream)
-            torch.cuda.synchronize()
-            cold.append(s0.elapsed_time(s1))
-        del flush
-        cold.sort()
-
-    flops_step = (18 if backward else 6) * P * H * I
-    tflops = flops_step / (ms * 1e-3) / 1e12
-    dom_flops = GEMM_FLOPS[dominant] * P * H * I
-    dom_tflops = dom_flops / (dom_ms * 1e-3) / 1e12
-    active = int((np.bincount(d["topk_idx"][d["topk_idx"] >= 0].ravel(), minlength=E) > 0).sum())
-    dom_bytes = gemm_bytes(dominant, N, H, I, P, active)
-    # the roofline that bounds the kernel: HBM below the ridge intensity (decode), else MFMA
-    hbm_bound = dom_flops / dom_bytes < RIDGE
-    traffic = counted_traffic(dominant, args.workload)
-    if hbm_bound:
-        roof = {"kernel": dominant, "bound": "hbm",
-                "achieved": round(dom_bytes / (dom_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBPS,
-                "unit": "GB/s", "frac": round(dom_bytes / (dom_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
-    else:
-        roof = {"kernel": dominant, "bound": "mfma", "achieved": round(dom_tflops, 2),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4)}
-    roof.update({"traffic": traffic, "avg_us": round(dom_ms * 1e3, 2),
-                 "flops_per_launch": dom_flops, "bytes_per_launch": dom_bytes,
-                 "intensity_flop_per_byte": round(dom_flops / dom_bytes, 1)})
-
+    backward = synth.CONFIGS[args.workload]["backward"]
     res = {
         "metric": METRIC,
-        "value": round(tflops, 2),
+        "value": r["TFLOPs"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": r["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "N": N, "H": H, "I": I, "E": E, "K": K, "P": P,
-                   "seed": d["seed"],
-                   "step": "metadata + forward" + (" + backward" if backward else ""),
-                   "flops_per_step": flops_step},
-        "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-        "cold": ({"ms_per_step": round(cold[len(cold) // 2], 4),
-                  "TFLOPs": round(flops_step / (cold[len(cold) // 2] * 1e-3) / 1e12, 2),
-                  "reps": len(cold)} if cold else None),
+        "config": {"workload": args.workload, "N": N, "H": r["H"], "I": r["I"], "E": E, "K": K,
+                   "P": P, "seed": r["seed"], "step": r["step"],
+                   "flops_per_step": r["flops_per_step"]},
+        "timing": "median of per-step event times over the timed steps",
+        "mean_ms_per_step": r["mean_ms_per_step"],
+        "mfma_frac": r["mfma_frac"],
+        "cold": r["cold"],
         "metadata": {"us": round(meta_us, 2), "eager_us": round(meta_eager_us, 2),
                      "bytes": meta_bytes,
                      "GBps": round(meta_bytes / (meta_us * 1e-6) / 1e9, 1),
                      "hbm_frac": round(meta_bytes / (meta_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)},
-        "kernels_us": {k: round(v, 1) for k, v in kernel_us.items()},
-        "roofline": roof,
-        "wall_s_timed": round(wall, 4),
+        "kernels_us": r["kernels_us"],
+        "roofline": r["roofline"],
+        "wall_s_timed": r["wall_s_timed"],
     }
+    del r
+    torch.cuda.empty_cache()
     res["router"] = router_timing(moe, synth, torch, np)
+    if not args.no_other_workloads:
+        others = {}
+        for name in ("dsv3_rank", "long_prefill", "decode"):
+            if name == args.workload:
+                continue
+            print(f"bench: {name}", file=sys.stderr, flush=True)
+            ro, _ = measure(moe, synth, torch, np, name, args.seed, args.other_steps, 3, 0,
+                            stream)
+            handles = ro.pop("_handles")
+            ro.pop("cold")
+            if not synth.CONFIGS[name]["backward"]:
+                ro["metadata_us"] = round(metadata_alone(torch, moe, handles, stream)[0], 2)
+            del handles
+            others[name] = ro
+            torch.cuda.empty_cache()
+        res["workloads"] = others
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(d, backward, args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -58,9 +58,6 @@ typedef enum {
   MOE_FP32 = 1  /* fp32 storage and arithmetic: the checking mode */
 } moe_dtype;
 
-/* Column order of W_up's 2I output columns. The Hysen Labs page on
- * Dao-AILab/sonic-moe ("Interleaved by default, concatenated if your model is
- * HuggingFace") gives the interleaved order gate0, up0, gate1, up1, ... */
 /* Column order of W_up [E,H,2I] (and of dW_up):
  *  INTERLEAVED: column 2j = gate_j, 2j+1 = up_j (the Hysen Labs page on SonicMoE: the
  *               interleaved format is the default);
@@ -192,13 +189,13 @@ typedef enum {
 } moe_kernel_id;
 
 /* After this call, the i-th launch of `kernel` (i < n_launches, counted from this
- * call) is bracketed by hipEventRecord(events[2i]) just before it and
- * hipEventRecord(events[2i+1]) just after it, on the launch's stream. events
- * holds 2*n_launches hipEvent_t created by the caller (none NULL, else
- * MOE_EINVAL); events == NULL stops
- * recording. Process-wide state, not thread-safe; for benchmarks only.
- * Returns the number of launches bracketed since the previous call through
- * *n_recorded (may be NULL). */
+ * call) made by the calling host thread is bracketed by hipEventRecord(events[2i])
+ * just before it and hipEventRecord(events[2i+1]) just after it, on the launch's
+ * stream. events holds 2*n_launches hipEvent_t created by the caller (none NULL,
+ * else MOE_EINVAL); events == NULL stops recording. The hook is per host thread:
+ * launches made by other threads are never bracketed and never touch it. For
+ * benchmarks only. Returns the number of launches bracketed since the previous call
+ * (from this thread) through *n_recorded (may be NULL). */
 moe_status moe_time_kernel(moe_kernel_id kernel, void *const *events, int32_t n_launches,
                            int32_t *n_recorded);
 const char *moe_kernel_name(moe_kernel_id kernel);

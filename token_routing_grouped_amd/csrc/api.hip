@@ -61,12 +61,15 @@ BwdWs bwd_layout(const moe_metadata *m, int32_t H, int32_t I, moe_dtype dt) {
   return w;
 }
 
-// ---- diagnostics: events around the launches of one kernel
+// ---- diagnostics: events around the launches of one kernel. The hook belongs to the
+// host thread that armed it (thread-local): launches made by other threads never read
+// or advance it, so arming it in one thread cannot race with another thread's calls.
 struct TimingHook {
   int kernel = -1;
   hipEvent_t const *events = nullptr;
   int n = 0, i = 0;
-} g_hook;
+};
+thread_local TimingHook g_hook;
 
 struct Bracket {  // records the start event on construction, the end event on destruction
   hipStream_t st;
@@ -117,6 +120,31 @@ static MetaOut meta_out(const moe_metadata *meta) {
 }
 }  // namespace moe
 
+namespace {
+// The three metadata launches over an argument-checked metadata object and a workspace
+// of at least meta_workspace_bytes(N*K, E) bytes. None of the workspace needs to start
+// zeroed: every cell the kernels read was written earlier in the same build.
+moe_status enqueue_metadata(const int32_t *topk_idx, const float *topk_weights,
+                            const moe_metadata *meta, int32_t *ws, hipStream_t st) {
+  const MetaOut o = meta_out(meta);
+  hipError_t err;
+  {
+    Bracket b(MOE_KERNEL_META_HIST, st);
+    err = launch_meta_hist(topk_idx, meta->N, meta->K, meta->E, ws, st);
+  }
+  if (err != hipSuccess) return MOE_EHIP;
+  {
+    Bracket b(MOE_KERNEL_META_SCAN, st);
+    err = launch_meta_scan(meta->N, meta->K, meta->E, ws, st);
+  }
+  if (err != hipSuccess) return MOE_EHIP;
+  Bracket b(MOE_KERNEL_META_SCATTER, st);
+  err = launch_meta_scatter(topk_idx, topk_weights, meta->N, meta->K, meta->E, meta->capacity,
+                            ws, o, st);
+  return err == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+}  // namespace
+
 extern "C" {
 
 size_t moe_build_metadata_workspace(int32_t N, int32_t K, int32_t E) {
@@ -144,23 +172,8 @@ moe_status moe_build_metadata(const int32_t *topk_idx, const float *topk_weights
   if (NK > 0 && (!topk_idx || !topk_weights)) return MOE_EINVAL;
   const size_t need = meta_workspace_bytes(NK, meta->E);
   if (workspace_bytes < need || !workspace) return MOE_ENOSPC;
-  const MetaOut o = meta_out(meta);
-  hipStream_t st = (hipStream_t)stream;
-  hipError_t err;
-  {
-    Bracket b(MOE_KERNEL_META_HIST, st);
-    err = launch_meta_hist(topk_idx, meta->N, meta->K, meta->E, (int32_t *)workspace, st);
-  }
-  if (err != hipSuccess) return MOE_EHIP;
-  {
-    Bracket b(MOE_KERNEL_META_SCAN, st);
-    err = launch_meta_scan(meta->N, meta->K, meta->E, (int32_t *)workspace, st);
-  }
-  if (err != hipSuccess) return MOE_EHIP;
-  Bracket b(MOE_KERNEL_META_SCATTER, st);
-  err = launch_meta_scatter(topk_idx, topk_weights, meta->N, meta->K, meta->E, meta->capacity,
-                            (const int32_t *)workspace, o, st);
-  return err == hipSuccess ? MOE_OK : MOE_EHIP;
+  return enqueue_metadata(topk_idx, topk_weights, meta, (int32_t *)workspace,
+                          (hipStream_t)stream);
 }
 
 size_t moe_route_workspace(int32_t N, int32_t K, int32_t E) {

@@ -1,7 +1,14 @@
-// fp32 checking mode of the grouped GEMMs: the same schedules, row maps and
-// epilogues as the bf16 matrix-core kernels, with fp32 storage and fp32 FMA
-// arithmetic, so indexing and epilogue mistakes show up at fp32 tolerance
-// instead of hiding under bf16 rounding. Not tuned for speed.
+// fp32 checking mode of the grouped GEMMs: fp32 storage and fp32 FMA arithmetic, so
+// the method's indexing and epilogue arithmetic can be checked at fp32 tolerance
+// instead of under bf16 rounding. Shared with the bf16 matrix-core kernels: the row
+// maps (x_gather_idx, sorted positions, the expert segments of
+// expert_frequency_offset), the per-expert row tiles found from the offsets on the
+// device, and the epilogue formulas (SwiGLU; dSwiGLU with the router weight and the
+// per-column-tile dscore partials; exact zeros for experts with no rows). Not shared:
+// the tile schedules (one non-persistent 128x128 workgroup per tile, weight-gradient
+// tiles dealt out flat rather than per XCD) and the store paths (direct per-lane
+// stores, no LDS staging or lane exchanges), so a pass here says nothing about those
+// parts of the bf16 kernels. Not tuned for speed.
 #include "common.h"
 #include "kernels.h"
 #include "../../include/moe.h"
