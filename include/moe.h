@@ -113,6 +113,23 @@ moe_status moe_build_metadata(const int32_t *topk_idx, const float *topk_weights
                               const moe_metadata *meta, void *workspace,
                               size_t workspace_bytes, void *stream);
 
+/* Allocation-free variant of moe_build_metadata, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Same arguments without the workspace, same kernels and the same
+ * results: the workspace is a library-owned static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES on each GPU (held until the process ends), on the GPU
+ * current for the calling thread (the stream must belong to it). A build whose
+ * workspace would exceed that (moe_build_metadata_workspace(N, K, E) >
+ * MOE_NOALLOC_SCRATCH_BYTES) returns MOE_ENOSPC before anything is enqueued; argument
+ * errors as for moe_build_metadata; MOE_EHIP if the array's address cannot be found.
+ * Allocates and frees nothing. Every call on one GPU shares that GPU's array, which
+ * keeps the last call's contents (no part of it needs to start zeroed): calls that
+ * overlap on one GPU (other streams, or unordered host threads) race on it and must
+ * not be issued; calls ordered on one stream are safe. */
+enum { MOE_NOALLOC_SCRATCH_BYTES = 4 << 20 };
+moe_status moe_build_metadata_noalloc(const int32_t *topk_idx, const float *topk_weights,
+                                      const moe_metadata *meta, void *stream);
+
 /* Router top-K from logits, fused with the metadata build (the Hysen Labs page on
  * Dao-AILab/sonic-moe, section "Three routing strategies, selected on the command
  * line": softmax over the top-K logits, or top-K over the softmax of all experts with

@@ -1,0 +1,91 @@
+"""The allocation-free metadata build (moe_build_metadata_noalloc, for callers that
+cannot allocate device memory) against the workspace entry point moe_build_metadata:
+bit-identical metadata on two calls in a row, the second smaller than the first (the
+library's static scratch then holds the first call's contents), and a build larger
+than the scratch refused synchronously."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from _util import Gpu
+
+pytestmark = pytest.mark.gpu
+
+KEYS = ["expert_frequency", "expert_frequency_offset", "x_gather_idx", "s_scatter_idx",
+        "s_reverse_scatter_idx", "num_activated_expert_per_token_offset", "router_scores",
+        "status"]
+
+
+def both_ways(d, capacity=None):
+    """(workspace build, allocation-free build) of the same inputs, as numpy dicts."""
+    import token_routing_grouped_amd as moe
+
+    ga = Gpu(d, capacity=capacity)
+    ga.build()
+    gb = Gpu(d, capacity=capacity)
+    # poison the outputs so that a skipped write cannot pass
+    for t in (gb.meta.expert_frequency, gb.meta.expert_frequency_offset, gb.meta.x_gather_idx,
+              gb.meta.s_scatter_idx, gb.meta.s_reverse_scatter_idx,
+              gb.meta.num_activated_expert_per_token_offset, gb.meta.status):
+        t.fill_(-7)
+    gb.meta.router_scores.fill_(float("nan"))
+    moe.moe_build_metadata_noalloc(gb.topk_idx, gb.topk_weights, gb.meta)
+    ga.torch.cuda.synchronize()
+    return ga.meta_numpy(), gb.meta_numpy()
+
+
+def check_same(a, b, d):
+    for k in KEYS:
+        assert np.array_equal(a[k], b[k]), k
+    m = oracle.build_metadata(d["topk_idx"], d["topk_weights"], d["E"])
+    for k in KEYS[:-1]:
+        assert np.array_equal(b[k], m[k].astype(b[k].dtype)), k
+
+
+def test_noalloc_matches_workspace_build_twice():
+    import token_routing_grouped_amd as moe
+
+    big = synth.make_inputs("qwen3_rank", 0, dout=False)
+    big_ws = moe.moe_build_metadata_workspace(big["N"], big["K"], big["E"])
+    small = synth.case(N=700, H=128, I=128, E=12, K=3, seed=51, p_invalid=0.3)
+    small_ws = moe.moe_build_metadata_workspace(small["N"], small["K"], small["E"])
+    assert small_ws < big_ws <= moe.MOE_NOALLOC_SCRATCH_BYTES
+    print(f"noalloc call 1: N={big['N']} K={big['K']} E={big['E']} ({big_ws} bytes)", flush=True)
+    a, b = both_ways(big)
+    check_same(a, b, big)
+    print(f"noalloc call 2: N={small['N']} K={small['K']} E={small['E']} ({small_ws} bytes)",
+          flush=True)
+    a, b = both_ways(small)
+    check_same(a, b, small)
+
+
+def test_noalloc_over_capacity_and_bad_ids():
+    # data errors take the same device status path as the workspace build
+    d = synth.case(N=300, H=128, I=128, E=6, K=3, seed=52)
+    d["topk_idx"][5, 1] = 77
+    P = int(((d["topk_idx"] >= 0) & (d["topk_idx"] < 6)).sum())
+    print("noalloc: bad id and capacity below P", flush=True)
+    a, b = both_ways(d, capacity=P - 9)
+    assert a["status"] == b["status"] == 3
+    for k in KEYS:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_noalloc_refuses_builds_beyond_the_scratch():
+    import torch
+
+    import token_routing_grouped_amd as moe
+
+    # 1024 experts over 2^21 slots need more workspace than the static scratch holds
+    N, K, E = 1 << 18, 8, 1024
+    assert moe.moe_build_metadata_workspace(N, K, E) > moe.MOE_NOALLOC_SCRATCH_BYTES
+    meta = moe.Metadata(N, K, E, 16, device="cuda")
+    idx = torch.full((N, K), -1, dtype=torch.int32, device="cuda")
+    w = torch.zeros((N, K), dtype=torch.float32, device="cuda")
+    meta.status.fill_(-7)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_build_metadata_noalloc(idx, w, meta)
+    assert ei.value.status == moe._binding.MOE_ENOSPC
+    torch.cuda.synchronize()
+    assert int(meta.status.item()) == -7  # nothing was enqueued

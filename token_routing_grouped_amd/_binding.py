@@ -24,8 +24,9 @@ EXPORTED_SYMBOLS = [
     "moe_build_metadata_workspace", "moe_expert_forward_workspace",
     "moe_expert_backward_workspace", "moe_build_metadata", "moe_expert_forward",
     "moe_expert_backward", "moe_status_string", "moe_time_kernel", "moe_kernel_name",
-    "moe_route_workspace", "moe_route",
+    "moe_route_workspace", "moe_route", "moe_build_metadata_noalloc",
 ]
+MOE_NOALLOC_SCRATCH_BYTES = 4 << 20
 KERNELS = ["meta_hist", "meta_scan", "meta_scatter", "up_swiglu", "down", "combine", "down_bwd",
            "wgrad_down", "up_bwd", "wgrad_up", "combine_dx", "route"]
 MOE_ROUTE_SOFTMAX_TOPK, MOE_ROUTE_TOPK_SOFTMAX = 0, 1
@@ -69,6 +70,8 @@ def lib():
         L.moe_expert_backward_workspace.argtypes = [vp, i32, i32, ctypes.c_int]
         L.moe_build_metadata.restype = ctypes.c_int
         L.moe_build_metadata.argtypes = [vp, vp, vp, vp, sz, vp]
+        L.moe_build_metadata_noalloc.restype = ctypes.c_int
+        L.moe_build_metadata_noalloc.argtypes = [vp, vp, vp, vp]
         L.moe_expert_forward.restype = ctypes.c_int
         L.moe_expert_forward.argtypes = [vp, vp, vp, vp, i32, i32, ctypes.c_int, ctypes.c_int,
                                          vp, vp, vp, sz, vp]
@@ -204,6 +207,18 @@ def moe_build_metadata(topk_idx, topk_weights, meta: Metadata, workspace=None, s
         _check(lib().moe_build_metadata(pi, pw, meta.ptr, ws, nb, _stream(stream)),
                "moe_build_metadata")
     return wst
+
+
+def moe_build_metadata_noalloc(topk_idx, topk_weights, meta: Metadata, stream=None):
+    """moe_build_metadata with the library's static per-GPU scratch as its workspace:
+    allocates nothing (raises MoeError with MOE_ENOSPC when the build needs more than
+    MOE_NOALLOC_SCRATCH_BYTES). Calls overlapping on one GPU race on that scratch."""
+    N, K = meta.N, meta.K
+    pi = _dev_on(meta, topk_idx, "topk_idx", torch.int32, (N, K))
+    pw = _dev_on(meta, topk_weights, "topk_weights", torch.float32, (N, K))
+    with _on(meta, stream):
+        _check(lib().moe_build_metadata_noalloc(pi, pw, meta.ptr, _stream(stream)),
+               "moe_build_metadata_noalloc")
 
 
 def moe_route_workspace(N: int, K: int, E: int) -> int:

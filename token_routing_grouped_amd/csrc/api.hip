@@ -3,6 +3,9 @@
 // frees, synchronises or reads device memory.
 #include <limits.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/moe.h"
 #include "kernels.h"
 
@@ -103,6 +106,33 @@ moe_status gemm(GemmKind kind, moe_kernel_id id, const GemmArgs &g, moe_dtype dt
   return err == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
+// ---- the library-owned scratch of the allocation-free metadata build. A file-scope
+// device array: each GPU the library runs on holds its own copy, at its own address,
+// until the process ends. In host code `scratch` is only a stand-in for the symbol;
+// the device address of the current GPU's copy is looked up once per device
+// (hipGetSymbolAddress, with that device current) and kept, and only that address is
+// ever passed to kernels.
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) int32_t scratch[MOE_NOALLOC_SCRATCH_BYTES / sizeof(int32_t)];
+std::atomic<int32_t *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int32_t *scratch_of_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  int32_t *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    void *addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return nullptr;
+    p = (int32_t *)addr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
 }  // namespace
 
 namespace moe {
@@ -174,6 +204,17 @@ moe_status moe_build_metadata(const int32_t *topk_idx, const float *topk_weights
   if (workspace_bytes < need || !workspace) return MOE_ENOSPC;
   return enqueue_metadata(topk_idx, topk_weights, meta, (int32_t *)workspace,
                           (hipStream_t)stream);
+}
+
+moe_status moe_build_metadata_noalloc(const int32_t *topk_idx, const float *topk_weights,
+                                      const moe_metadata *meta, void *stream) {
+  if (!meta_ok(meta)) return MOE_EINVAL;
+  const int64_t NK = (int64_t)meta->N * meta->K;
+  if (NK > 0 && (!topk_idx || !topk_weights)) return MOE_EINVAL;
+  if (meta_workspace_bytes(NK, meta->E) > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ENOSPC;
+  int32_t *ws = scratch_of_current_device();
+  if (!ws) return MOE_EHIP;
+  return enqueue_metadata(topk_idx, topk_weights, meta, ws, (hipStream_t)stream);
 }
 
 size_t moe_route_workspace(int32_t N, int32_t K, int32_t E) {
