@@ -157,20 +157,22 @@ namespace {
 moe_status enqueue_metadata(const int32_t *topk_idx, const float *topk_weights,
                             const moe_metadata *meta, int32_t *ws, hipStream_t st) {
   const MetaOut o = meta_out(meta);
+  // few chunks and experts: the scatter pass sums the chunk counts itself (two launches)
+  const bool fused = meta_fused_scan((int64_t)meta->N * meta->K, meta->E);
   hipError_t err;
   {
     Bracket b(MOE_KERNEL_META_HIST, st);
     err = launch_meta_hist(topk_idx, meta->N, meta->K, meta->E, ws, st);
   }
   if (err != hipSuccess) return MOE_EHIP;
-  {
+  if (!fused) {
     Bracket b(MOE_KERNEL_META_SCAN, st);
     err = launch_meta_scan(meta->N, meta->K, meta->E, ws, st);
   }
   if (err != hipSuccess) return MOE_EHIP;
   Bracket b(MOE_KERNEL_META_SCATTER, st);
   err = launch_meta_scatter(topk_idx, topk_weights, meta->N, meta->K, meta->E, meta->capacity,
-                            ws, o, st);
+                            ws, o, st, fused);
   return err == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 }  // namespace

@@ -181,19 +181,35 @@ void gemm_bf16_kernel(GemmArgs g) {
       s_order[rank] = i;
     }
     __syncthreads();
+    // An expert's tile grid (mtn x ntn) is cut into xa row bands x xb column bands, one
+    // rectangle per XCD: an XCD then reads the A columns of its row band and the B
+    // columns of its column band, so the bytes all XCDs fetch per reduction row are
+    // xb * M + xa * N; the cut with the fewest is taken (ties: more row bands). Grids
+    // that no cut divides are dealt out flat.
     const int mtn = g.M / BM, ntn = g.N / BN, tpe = mtn * ntn;
-    int rank, tile;
-    if (tpe % kNumXcd == 0) {
+    int xa = 0, xb = 0;
+    for (int a = kNumXcd; a >= 1; a >>= 1) {
+      const int b = kNumXcd / a;
+      if (mtn % a || ntn % b) continue;
+      if (!xa || (int64_t)b * g.M + (int64_t)a * g.N < (int64_t)xb * g.M + (int64_t)xa * g.N) {
+        xa = a;
+        xb = b;
+      }
+    }
+    int rank;
+    if (xa) {
       const int c = tpe / kNumXcd, x = blockIdx.x % kNumXcd, i = blockIdx.x / kNumXcd;
       rank = i / c;
-      tile = x * c + (i - rank * c);
+      const int l = i - rank * c, bn = ntn / xb;  // tile l of this XCD's rectangle
+      mt = (x / xb) * (mtn / xa) + l / bn;
+      nt = (x % xb) * bn + l % bn;
     } else {
       rank = blockIdx.x / tpe;
-      tile = blockIdx.x - rank * tpe;
+      const int tile = blockIdx.x - rank * tpe;
+      mt = tile / ntn;
+      nt = tile - mt * ntn;
     }
     e = s_order[rank];
-    mt = tile / ntn;
-    nt = tile - mt * ntn;
     seg0 = g.foff[e];
     seglen = P > g.cap ? 0 : g.foff[e + 1] - seg0;
     nk = (seglen + BK - 1) / BK;
@@ -660,73 +676,92 @@ void gemm_bf16_kernel(GemmArgs g) {
     const uint16_t *__restrict__ Hs = (const uint16_t *)g.Hs;
     float *red = (float *)smem;  // [WGN][BM] row partials of the column waves (the
                                  // loop's final barrier has released the stages)
-    // The saved (gate, up) pairs of the next (mi, ni) block are loaded while the current
-    // block is computed: each register is refilled right after its value is consumed, so
-    // one block of loads is always in flight. Rows past the segment read row 0 of the
-    // tile and are never stored.
-    uint32_t hv[16];
-    auto h_addr = [&](int mi_, int ni_, int r) {
-      const int j_ = nt * BN + wn * WN + ni_ * 32 + col_l;
-      const int row_ = wm * WM + mi_ * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+    // Adjacent lanes (one column each) exchange their values of rows r and r+1 with one
+    // DPP quad_perm [1,0,3,2] move per value (as in the plain-store epilogue): the even
+    // lane of a pair then holds columns (jb, jb+1) of row r, the odd lane those of row
+    // r+1, so each lane loads the two columns' saved (gate, up) pairs as 8 bytes and
+    // stores 8 bytes of dh and 4 of w*a per row pair. The saved pairs of the next
+    // (mi, ni) block are loaded while the current block is computed (each register is
+    // refilled right after its value is consumed). Rows past the segment read row 0 of
+    // the tile and are never stored.
+    const bool odd = lane & 1;
+    u32x2 hv[8];
+    auto h_addr = [&](int mi_, int ni_, int rp) {
+      const int jb_ = nt * BN + wn * WN + ni_ * 32 + (col_l & ~1);
+      const int r = 2 * rp;
+      const int row_ = wm * WM + mi_ * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3) + odd;
       const int64_t s_ = row0 + (row_ < rows ? row_ : 0);
-      return (const uint32_t *)(Hs + s_ * g.ldh + 2 * j_);
+      return (const u32x2 *)(Hs + s_ * g.ldh + 2 * jb_);
     };
 #pragma unroll
-    for (int r = 0; r < 16; r++) hv[r] = *h_addr(0, 0, r);
+    for (int rp = 0; rp < 8; rp++) hv[rp] = *h_addr(0, 0, rp);
 #pragma unroll
     for (int mi = 0; mi < TM; mi++) {
-      float part[16];
+      float pp[8];  // this lane's row of each row pair: its two columns' dscore terms
 #pragma unroll
-      for (int r = 0; r < 16; r++) part[r] = 0.0f;
+      for (int rp = 0; rp < 8; rp++) pp[rp] = 0.0f;
 #pragma unroll
       for (int ni = 0; ni < TN; ni++) {
         constexpr int NB = TM * TN;
         const int b = mi * TN + ni;
-        const int j = nt * BN + wn * WN + ni * 32 + col_l;
+        const int jb = nt * BN + wn * WN + ni * 32 + (col_l & ~1);
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-          const int row = wm * WM + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        for (int rp = 0; rp < 8; rp++) {
+          const int r = 2 * rp;
+          const float a0 = acc[mi][ni][r], a1 = acc[mi][ni][r + 1];
+          const float n0 = __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp(
+              (int)__float_as_uint(a0), 0xB1, 0xF, 0xF, false));
+          const float n1 = __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp(
+              (int)__float_as_uint(a1), 0xB1, 0xF, 0xF, false));
+          const float dau0 = odd ? n1 : a0;  // column jb of this lane's row
+          const float dau1 = odd ? a1 : n0;  // column jb + 1
+          const int row = wm * WM + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3) + odd;
           const int64_t srow = row0 + row;
           const float wq = s_wq[row];
-          const uint32_t h2 = hv[r];
-          if (b + 1 < NB) hv[r] = *h_addr((b + 1) / TN, (b + 1) % TN, r);
-          const float gt = bf16_to_f32((uint16_t)(h2 & 0xffffu));
-          const float up = bf16_to_f32((uint16_t)(h2 >> 16));
-          const float dau = acc[mi][ni][r];
-          const float sg = sigmoid_fast(gt);
-          const float a = gt * sg * up;
+          const u32x2 h4 = hv[rp];
+          if (b + 1 < NB) hv[rp] = *h_addr((b + 1) / TN, (b + 1) % TN, rp);
+          const float gt0 = bf16_to_f32((uint16_t)(h4[0] & 0xffffu));
+          const float up0 = bf16_to_f32((uint16_t)(h4[0] >> 16));
+          const float gt1 = bf16_to_f32((uint16_t)(h4[1] & 0xffffu));
+          const float up1 = bf16_to_f32((uint16_t)(h4[1] >> 16));
+          const float sg0 = sigmoid_fast(gt0), sg1 = sigmoid_fast(gt1);
+          const float av0 = gt0 * sg0 * up0, av1 = gt1 * sg1 * up1;
           if (row < rows) {
-            part[r] += dau * a;
-            const float da = wq * dau;
-            const float dg = da * up * sg * (1.0f + gt * (1.0f - sg));
-            const float du = da * gt * sg;
+            pp[rp] += dau0 * av0 + dau1 * av1;
+            const float da0 = wq * dau0, da1 = wq * dau1;
+            const float dg0 = da0 * up0 * sg0 * (1.0f + gt0 * (1.0f - sg0));
+            const float dg1 = da1 * up1 * sg1 * (1.0f + gt1 * (1.0f - sg1));
+            const float du0 = da0 * gt0 * sg0, du1 = da1 * gt1 * sg1;
             if (g.gu_concat) {  // dh in W_up's column order
-              dH[srow * g.ldc + j] = f32_to_bf16(dg);
-              dH[srow * g.ldc + g.N + j] = f32_to_bf16(du);
+              *(uint32_t *)(dH + srow * g.ldc + jb) = pack_bf16x2(dg0, dg1);
+              *(uint32_t *)(dH + srow * g.ldc + g.N + jb) = pack_bf16x2(du0, du1);
             } else {
-              *(uint32_t *)(dH + srow * g.ldc + 2 * j) = pack_bf16x2(dg, du);
+              *(u32x2 *)(dH + srow * g.ldc + 2 * jb) =
+                  u32x2{pack_bf16x2(dg0, du0), pack_bf16x2(dg1, du1)};
             }
-            AW[srow * g.ldc2 + j] = f32_to_bf16(wq * a);
+            *(uint32_t *)(AW + srow * g.ldc2 + jb) = pack_bf16x2(wq * av0, wq * av1);
           }
         }
       }
-      // butterfly over the 32 lanes of each half: after exchanging half of the
-      // values at each step, lane l holds the full row sum for r = (l%32)/2
+      // Row sums over the 32 columns: lanes of one parity hold the same row of each
+      // pair, so the butterfly runs over lane bits 4, 3, 2 (halving the entries each
+      // step) and then adds the lane two apart; lane l then holds the row sum of entry
+      // (l % 32) / 4 for its parity.
 #pragma unroll
-      for (int n = 16, o = 16; n > 1; n >>= 1, o >>= 1) {
+      for (int n = 8, o = 16; n > 1; n >>= 1, o >>= 1) {
         const bool upper = (lane & o) != 0;
 #pragma unroll
         for (int i = 0; i < n / 2; i++) {
-          const float send = upper ? part[i] : part[i + n / 2];
-          const float keep = upper ? part[i + n / 2] : part[i];
-          part[i] = keep + __shfl_xor(send, o, kWave);
+          const float send = upper ? pp[i] : pp[i + n / 2];
+          const float keep = upper ? pp[i + n / 2] : pp[i];
+          pp[i] = keep + __shfl_xor(send, o, kWave);
         }
       }
-      const float rsum = part[0] + __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(
-                                       0, (int)__float_as_uint(part[0]), 0xB1, 0xF, 0xF, false));
-      const int rr = (lane & 31) >> 1;
+      const float rsum = pp[0] + __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(
+                                     0, (int)__float_as_uint(pp[0]), 0x4E, 0xF, 0xF, false));
+      const int rr = 2 * ((lane & 31) >> 2) + odd;
       const int row = wm * WM + mi * 32 + (rr >> 2) * 8 + (lane >> 5) * 4 + (rr & 3);
-      if ((lane & 1) == 0) red[wn * BM + row] = rsum;
+      if ((lane & 2) == 0) red[wn * BM + row] = rsum;
     }
     __syncthreads();
     for (int r = tid; r < rows; r += NT) {
@@ -787,48 +822,6 @@ hipError_t launch_tiles(int bm, int bn, int bk, int grid, const GemmArgs &g, hip
 }
 
 }  // namespace
-
-// Tile shape per GEMM: 256x256x32 with eight waves where the fixed dimensions allow it
-// (half the bytes per flop of 128x128), else 128x128; 32x128x64 with two waves when the
-// capacity averages at most 16 rows per expert.
-#ifndef MOE_GM_BIG
-#define MOE_GM_BIG 1
-#endif
-#ifndef MOE_VK_BIG
-#define MOE_VK_BIG 1
-#endif
-#ifndef MOE_TILE_GM_BK
-#define MOE_TILE_GM_BK 64
-#endif
-#ifndef MOE_TILE_VK_BK
-#define MOE_TILE_VK_BK 32
-#endif
-
-void gemm_tile(GemmKind kind, const GemmArgs &g, int *bm, int *bn, int *bk) {
-  if (kind == kWeightGrad) {
-    const bool big = MOE_VK_BIG && g.M % 256 == 0 && g.N % 256 == 0;
-    *bm = big ? 256 : 128;
-    *bn = big ? 256 : 128;
-    *bk = big ? 32 : MOE_TILE_VK_BK;
-  } else {
-    // few rows per expert (decode): 32-row tiles, so the matrix work per streamed
-    // weight byte matches the rows there are and many more workgroups stream weights
-    const bool skinny = (int64_t)g.cap <= 16LL * g.E && g.N % 128 == 0 && g.K % 64 == 0;
-    const bool big = MOE_GM_BIG && g.N % 256 == 0 && g.K % 32 == 0;
-    *bm = skinny ? 32 : big ? 256 : 128;
-    *bn = skinny ? 128 : big ? 256 : 128;
-    *bk = skinny ? 64 : big ? 32 : (g.K % MOE_TILE_GM_BK == 0 ? MOE_TILE_GM_BK : 32);
-  }
-}
-
-int gemm_grid(GemmKind kind, const GemmArgs &g) {
-  int bm, bn, bk;
-  gemm_tile(kind, g, &bm, &bn, &bk);
-  if (kind == kWeightGrad) return g.E * (g.M / bm) * (g.N / bn);
-  const int64_t mt = ((int64_t)g.cap + (int64_t)g.E * (bm - 1)) / bm;
-  const int64_t grid = mt * (g.N / bn);
-  return grid > 0x7fffffff ? -1 : (int)grid;
-}
 
 hipError_t launch_gemm_bf16(GemmKind kind, const GemmArgs &g, hipStream_t st) {
   const int grid = gemm_grid(kind, g);

@@ -17,7 +17,9 @@
 //     inside wavefronts), stored row-major [nblk][E+2], and the column total; long
 //     columns take a first pass of segment sums.
 //  3. meta_scatter: each workgroup reads its row of prefixes and the totals (one
-//     memory round trip), scans the totals into expert_frequency_offset, then
+//     memory round trip; with at most 256 chunks and 34 experts it instead sums the
+//     count columns itself and the scan launch is skipped, a two-launch build), scans
+//     the totals into expert_frequency_offset, then
 //     ranks its own slots stably: inside a wavefront the lanes holding the same
 //     expert are found with one ballot per expert-id bit and ranked with mbcnt;
 //     per-wave running counts in LDS order the rounds and the four waves. Every
@@ -150,9 +152,17 @@ __global__ __launch_bounds__(kMetaThreads) void meta_scan_kernel(
   if (tid == 0 && seg == nseg - 1) tot[c] = s_base + t;
 }
 
+// Limits of the scatter pass that scans the chunk counts itself (FUSED): at most
+// kFusedCols columns per wavefront of a four-wavefront workgroup (E + 2 <= 36) and
+// kFusedChunks chunks, so every count a workgroup needs is loaded at once.
+constexpr int kFusedCols = 9, kFusedChunks = 256;
+
 // NW wavefronts per workgroup; each ranks ITEMS rounds of 64 slots of its share of the
-// chunk (the 2048-slot chunks take 8 wavefronts, so a wavefront's rounds stay at 4)
-template <int ITEMS, int NW>
+// chunk (the 2048-slot chunks take 8 wavefronts, so a wavefront's rounds stay at 4).
+// FUSED: `pre` is the per-chunk count columns [E+2][nblk] (nblk = the grid) and `tot` is
+// unused; each workgroup sums the counts of the chunks before its own and of all chunks
+// itself, so the build needs no separate scan launch.
+template <int ITEMS, int NW, bool FUSED>
 __global__ __launch_bounds__(64 * NW) void meta_scatter_kernel(
     const int32_t *__restrict__ idx, const float *__restrict__ wts, int N, int K, int E,
     int nbits, int cap, const int32_t *__restrict__ pre, const int32_t *__restrict__ tot,
@@ -196,16 +206,52 @@ __global__ __launch_bounds__(64 * NW) void meta_scatter_kernel(
     r_e[it] = j < NK ? idx[j] : -1;
     r_w[it] = j < NK ? wts[j] : 0.0f;
   }
-  const int32_t *prow = pre + (int64_t)me * W;
   const bool aux = me == 0 && out.aux;  // router: the load-balancing loss
   float *s_prod = (float *)(s_pq + CHUNK);  // [E] (router only)
-  for (int c = tid; c < W; c += NT) {
-    s_base[c] = prow[c];
-    if (c <= E) {
-      const int t = tot[c];
-      s_off[c < E ? c : E + 1] = t;
-      if (me == 0 && c < E) out.expert_frequency[c] = t;
-      if (aux && c < E) s_prod[c] = out.psum ? (float)t * out.psum[c] : 0.0f;
+  if constexpr (FUSED) {
+    // wavefront w sums columns w, w + NW, ...: all of its counts are loaded first (one
+    // memory round trip), then per column the chunks before this one and all chunks,
+    // each by a DPP wavefront scan
+    static_assert(NW == 4, "fused scan layout");
+    const int nblk = gridDim.x;
+    int v[kFusedCols][kFusedChunks / kWave];
+#pragma unroll
+    for (int ci = 0; ci < kFusedCols; ci++)
+#pragma unroll
+      for (int bi = 0; bi < kFusedChunks / kWave; bi++) {
+        const int c = w + ci * NW, b = lane + bi * kWave;
+        v[ci][bi] = (c < W && b < nblk) ? pre[(int64_t)c * nblk + b] : 0;
+      }
+#pragma unroll
+    for (int ci = 0; ci < kFusedCols; ci++) {
+      const int c = w + ci * NW;
+      if (c >= W) break;  // wave-uniform
+      int sb = 0, sa = 0;
+#pragma unroll
+      for (int bi = 0; bi < kFusedChunks / kWave; bi++) {
+        sa += v[ci][bi];
+        sb += lane + bi * kWave < me ? v[ci][bi] : 0;
+      }
+      sb = __builtin_amdgcn_readlane(wave_inclusive_scan_dpp(sb), kWave - 1);
+      sa = __builtin_amdgcn_readlane(wave_inclusive_scan_dpp(sa), kWave - 1);
+      if (lane == 0) {
+        s_base[c] = sb;
+        if (c <= E) {
+          s_off[c < E ? c : E + 1] = sa;
+          if (me == 0 && c < E) out.expert_frequency[c] = sa;
+        }
+      }
+    }
+  } else {
+    const int32_t *prow = pre + (int64_t)me * W;
+    for (int c = tid; c < W; c += NT) {
+      s_base[c] = prow[c];
+      if (c <= E) {
+        const int t = tot[c];
+        s_off[c < E ? c : E + 1] = t;
+        if (me == 0 && c < E) out.expert_frequency[c] = t;
+        if (aux && c < E) s_prod[c] = out.psum ? (float)t * out.psum[c] : 0.0f;
+      }
     }
   }
   for (int i = tid; i < NW * E + 8; i += NT) s_run[i] = 0;
@@ -356,9 +402,13 @@ hipError_t launch_meta_scan(int N, int K, int E, int32_t *ws, hipStream_t stream
   return hipGetLastError();
 }
 
+bool meta_fused_scan(int64_t NK, int E) {
+  return meta_items(NK) == 2 && E + 2 <= 4 * kFusedCols && meta_blocks(NK) <= kFusedChunks;
+}
+
 hipError_t launch_meta_scatter(const int32_t *topk_idx, const float *topk_weights, int N, int K,
                                int E, int capacity, const int32_t *ws, const MetaOut &out,
-                               hipStream_t stream) {
+                               hipStream_t stream, bool fused) {
   const int64_t NK = (int64_t)N * K;
   const MetaWs L = meta_ws_layout(NK, E);
   int nbits = 0;
@@ -367,21 +417,29 @@ hipError_t launch_meta_scatter(const int32_t *topk_idx, const float *topk_weight
   const int nw = items == 8 ? 8 : 4;  // wavefronts of the scatter workgroup
   const size_t sh = (size_t)(2 * (E + 2) + nw * E + 8 + (E + 1) + 3 * meta_chunk(NK) +
                              (out.aux ? E : 0)) * sizeof(int32_t);
-  if (items == 8) {
+  if (fused) {
+    if (!meta_fused_scan(NK, E) || out.aux) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((meta_scatter_kernel<2, 4, true>), dim3(L.nblk), dim3(64 * 4), sh, stream,
+                       topk_idx, topk_weights, N, K, E, nbits, capacity, ws + L.hist, nullptr,
+                       out);
+  } else if (items == 8) {
     // with 1024 experts the eight waves' running counts take the stage past the 64 KB of
     // dynamic LDS a launch gets by default (a workgroup may use up to 160 KB); set once
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&meta_scatter_kernel<4, 8>),
+        reinterpret_cast<const void *>(&meta_scatter_kernel<4, 8, false>),
         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((meta_scatter_kernel<4, 8>), dim3(L.nblk), dim3(64 * 8), sh, stream,
-                       topk_idx, topk_weights, N, K, E, nbits, capacity, ws + L.pre, ws + L.tot, out);
+    hipLaunchKernelGGL((meta_scatter_kernel<4, 8, false>), dim3(L.nblk), dim3(64 * 8), sh,
+                       stream, topk_idx, topk_weights, N, K, E, nbits, capacity, ws + L.pre,
+                       ws + L.tot, out);
   } else if (items == 4)
-    hipLaunchKernelGGL((meta_scatter_kernel<4, 4>), dim3(L.nblk), dim3(64 * 4), sh, stream,
-                       topk_idx, topk_weights, N, K, E, nbits, capacity, ws + L.pre, ws + L.tot, out);
+    hipLaunchKernelGGL((meta_scatter_kernel<4, 4, false>), dim3(L.nblk), dim3(64 * 4), sh,
+                       stream, topk_idx, topk_weights, N, K, E, nbits, capacity, ws + L.pre,
+                       ws + L.tot, out);
   else
-    hipLaunchKernelGGL((meta_scatter_kernel<2, 4>), dim3(L.nblk), dim3(64 * 4), sh, stream,
-                       topk_idx, topk_weights, N, K, E, nbits, capacity, ws + L.pre, ws + L.tot, out);
+    hipLaunchKernelGGL((meta_scatter_kernel<2, 4, false>), dim3(L.nblk), dim3(64 * 4), sh,
+                       stream, topk_idx, topk_weights, N, K, E, nbits, capacity, ws + L.pre,
+                       ws + L.tot, out);
   return hipGetLastError();
 }
 

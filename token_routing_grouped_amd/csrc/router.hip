@@ -284,7 +284,6 @@ __global__ __launch_bounds__(kRouteThreads) void route_hist_kernel(
 
 }  // namespace
 
-size_t route_ws_floats(int64_t NK, int E) { return (size_t)(meta_blocks(NK) + 1) * (size_t)E; }
 
 hipError_t launch_route_hist(const void *logits, bool bf16, int N, int E, int K, int mode,
                              int renorm, bool want_p, int32_t *topk_idx, float *topk_w,

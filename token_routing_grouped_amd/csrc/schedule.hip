@@ -1,0 +1,60 @@
+// Host-side size arithmetic of the kernels: tile shapes and grid sizes of the grouped
+// GEMMs and the router's workspace. Host code only (no kernels), so it can also be
+// built for the CPU alone and checked there under sanitizers.
+#include "kernels.h"
+
+namespace moe {
+
+// router workspace, in floats: per-chunk softmax sums [E][nblk], then their totals [E]
+size_t route_ws_floats(int64_t NK, int E) { return (size_t)(meta_blocks(NK) + 1) * (size_t)E; }
+
+// bf16 tiles: 256x256x32 with eight waves where the fixed dimensions allow it (half
+// the bytes per flop of 128x128), else 128x128; 32x128x64 with two waves when the
+// capacity averages at most 16 rows per expert (decode), so the matrix work per
+// streamed weight byte matches the rows there are and more workgroups stream weights.
+void gemm_tile(GemmKind kind, const GemmArgs &g, int *bm, int *bn, int *bk) {
+  if (kind == kWeightGrad) {
+    const bool big = g.M % 256 == 0 && g.N % 256 == 0;
+    *bm = big ? 256 : 128;
+    *bn = big ? 256 : 128;
+    *bk = 32;
+  } else {
+    const bool skinny = (int64_t)g.cap <= 16LL * g.E && g.N % 128 == 0 && g.K % 64 == 0;
+    const bool big = g.N % 256 == 0 && g.K % 32 == 0;
+    *bm = skinny ? 32 : big ? 256 : 128;
+    *bn = skinny ? 128 : big ? 256 : 128;
+    *bk = skinny ? 64 : big ? 32 : (g.K % 64 == 0 ? 64 : 32);
+  }
+}
+
+// Launch size: varlen-K launches one workgroup per output tile of every expert (-1
+// when that exceeds the grid limit); grouped-M returns an upper bound of its tiles
+// (row tiles of every expert segment, bounded from the capacity, times column tiles,
+// capped at INT_MAX), and the launch caps its persistent grid at what the chip holds.
+int gemm_grid(GemmKind kind, const GemmArgs &g) {
+  int bm, bn, bk;
+  gemm_tile(kind, g, &bm, &bn, &bk);
+  if (kind == kWeightGrad) {
+    const int64_t grid = (int64_t)g.E * (g.M / bm) * (g.N / bn);
+    return grid > 0x7fffffff ? -1 : (int)grid;
+  }
+  const int64_t mt = ((int64_t)g.cap + (int64_t)g.E * (bm - 1)) / bm;
+  const int64_t tiles = mt * (g.N / bn);
+  return tiles > 0x7fffffff ? 0x7fffffff : (int)tiles;
+}
+
+// fp32 checking mode: one workgroup per 128x128 tile (grouped-M: row tiles of every
+// expert segment, bounded from the capacity; varlen-K: every expert's output tiles);
+// -1 when that exceeds the grid limit.
+int gemm_grid_f32(GemmKind kind, const GemmArgs &g) {
+  int64_t grid;
+  if (kind == kWeightGrad) {
+    grid = (int64_t)g.E * (g.M / kGemmBM) * (g.N / kGemmBN);
+  } else {
+    const int64_t mt = ((int64_t)g.cap + (int64_t)g.E * (kGemmBM - 1)) / kGemmBM;
+    grid = mt * (g.N / kGemmBN);
+  }
+  return grid > 0x7fffffff ? -1 : (int)grid;
+}
+
+}  // namespace moe
