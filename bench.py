@@ -479,10 +479,18 @@ def main():
     if args.copy_mib:
         src = torch.ones(args.copy_mib << 20, dtype=torch.uint8, device="cuda:0")
         dst = torch.empty_like(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        dst.copy_(src)
+        e0.record()
         for _ in range(3):
             dst.copy_(src)
+        e1.record()
         torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes": args.copy_mib << 20, "launches": 3}))
+        ms = e0.elapsed_time(e1) / 3
+        nb = args.copy_mib << 20
+        # a copy moves its size twice (read and write)
+        print(json.dumps({"copy_bytes": nb, "launches": 4, "ms_per_copy": round(ms, 4),
+                          "GBps_read_plus_write": round(2 * nb / (ms * 1e-3) / 1e9, 1)}))
         return
 
     import synth

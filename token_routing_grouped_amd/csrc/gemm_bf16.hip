@@ -26,11 +26,9 @@
 // other reads fragments and stages the next tile. Operands whose reduction index is
 // contiguous in memory are stored [rows][BK] with 16-byte chunks swizzled per row and
 // read with 16-byte LDS loads; operands contiguous along M or N are stored as loaded,
-// [BK][cols+16], and read with ds_read_b64_tr_b16
-// (transposing LDS reads), so no operand is transposed in registers. The +16 padding is
-// the measured best for the transposing reads (94 B/clk per CU, against 83 with +32 and
-// 64 unpadded). Outputs are staged through LDS so every row leaves as whole 128-byte
-// lines.
+// [BK][cols+pad], and read with ds_read_b64_tr_b16 (transposing LDS reads), so no
+// operand is transposed in registers (the padding: padc below). Outputs are staged
+// through LDS so every row leaves as whole 128-byte lines.
 #include "common.h"
 #include "kernels.h"
 #include "../../include/moe.h"
@@ -43,7 +41,12 @@ namespace {
 #endif
 // extra elements per row of a reduction-contiguous tile [rows][BK] (0: chunk swizzle)
 constexpr int PADK = MOE_KC_SWIZZLE ? 0 : 8;
-constexpr int PADC = 16;  // extra columns of an M/N-contiguous tile [BK][cols]
+// extra columns of an M/N-contiguous tile [BK][cols]: 32 for 256-wide tiles (rows then
+// start 64 bytes apart modulo the 256-byte bank span, and the transposing fragment reads
+// of a wave run at 158-164 B/clk per CU against 128 with 16; measured on this part), 16
+// for narrower tiles, where 32 would cost the second workgroup per CU its LDS
+template <int R>
+constexpr int padc() { return R >= 256 ? 32 : 16; }
 
 enum { GROUPED_M = 0, VARLEN_K = 1 };
 // EPI_SWIGLU: W_up interleaved (gate_j, up_j at 2j, 2j+1); EPI_SWIGLU_CAT: [gates | ups]
@@ -53,8 +56,8 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 template <bool KC, int R, int BK>
 struct TileShape {  // one LDS stage of an operand with R rows (M or N) and BK reduction
-  static constexpr int ld = KC ? BK + PADK : R + PADC;
-  static constexpr int elems = KC ? R * (BK + PADK) : BK * (R + PADC);
+  static constexpr int ld = KC ? BK + PADK : R + padc<R>();
+  static constexpr int elems = KC ? R * (BK + PADK) : BK * (R + padc<R>());
 };
 
 // Reduction-contiguous tile [rows][BK], unpadded: 16-byte chunk c of row r is stored at
