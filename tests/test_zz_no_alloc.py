@@ -89,3 +89,59 @@ def test_noalloc_refuses_builds_beyond_the_scratch():
     assert ei.value.status == moe._binding.MOE_ENOSPC
     torch.cuda.synchronize()
     assert int(meta.status.item()) == -7  # nothing was enqueued
+
+
+def test_noalloc_build_in_a_hip_graph():
+    """The allocation-free build is what graph capture calls for: captured once (after a
+    first eager call has looked up the scratch address), replayed with two routings of one
+    shape loaded into the same input buffers, eager work and synchronisations between the
+    replays; every replay must equal, bit for bit, the workspace build of that routing."""
+    import torch
+
+    import token_routing_grouped_amd as moe
+
+    N, K, E = 3000, 8, 32
+    cases = [synth.make_inputs(dict(N=N, H=128, I=128, E=E, K=K, routing="ep_share",
+                                    global_experts=256), seed=s, dout=False)
+             for s in (3, 4)]
+    print(f"noalloc graph case N={N} K={K} E={E}", flush=True)
+    cap = N * K
+    idx = torch.empty(N, K, dtype=torch.int32, device="cuda")
+    wts = torch.empty(N, K, dtype=torch.float32, device="cuda")
+    meta = moe.Metadata(N, K, E, cap, device="cuda")
+    refs = []
+    for d in cases:
+        r = moe.Metadata(N, K, E, cap, device="cuda")
+        moe.moe_build_metadata(torch.from_numpy(d["topk_idx"]).cuda(),
+                               torch.from_numpy(d["topk_weights"]).cuda(), r)
+        torch.cuda.synchronize()
+        P = int(r.expert_frequency_offset[-1].item())
+        refs.append({k: getattr(r, k).cpu().numpy()[:P] if k in (
+            "x_gather_idx", "s_scatter_idx", "s_reverse_scatter_idx", "router_scores")
+            else getattr(r, k).cpu().numpy() for k in KEYS[:-1]})
+    idx.copy_(torch.from_numpy(cases[0]["topk_idx"]))
+    wts.copy_(torch.from_numpy(cases[0]["topk_weights"]))
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        moe.moe_build_metadata_noalloc(idx, wts, meta, stream=stream)  # eager: address lookup
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        moe.moe_build_metadata_noalloc(idx, wts, meta, stream=stream)
+    torch.cuda.synchronize()
+    for rep in range(6):
+        c = rep % 2
+        idx.copy_(torch.from_numpy(cases[c]["topk_idx"]))
+        wts.copy_(torch.from_numpy(cases[c]["topk_weights"]))
+        meta.x_gather_idx.fill_(-5)  # clobber between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert int(meta.status.item()) == 0
+        P = int(meta.expert_frequency_offset[-1].item())
+        for k, ref in refs[c].items():
+            got = getattr(meta, k).cpu().numpy()
+            if k in ("x_gather_idx", "s_scatter_idx", "s_reverse_scatter_idx", "router_scores"):
+                got = got[:P]
+            assert np.array_equal(got, ref), (rep, k)
