@@ -161,7 +161,9 @@ moe_status moe_route(const void *logits, moe_dtype logits_dtype, moe_route_mode 
  *              router_scores[q] * y[s_reverse_scatter_idx[q],:]   (fp32 sum)
  * Rows with no valid slot are 0. h_save [capacity,2I] (same dtype) receives h
  * for the backward; pass NULL for inference. out is [N,H].
- * Requires H % 128 == 0, I % 128 == 0. */
+ * H and I must be positive multiples of 8 (whole 16-byte bf16 chunks), at most
+ * 2^20; other sizes return MOE_EUNSUPPORTED. Sizes that are not multiples of the
+ * 128-wide tiles run with partial edge tiles. */
 moe_status moe_expert_forward(const moe_metadata *meta, const void *x, const void *w_up,
                               const void *w_down, int32_t H, int32_t I, moe_dtype dt,
                               moe_gateup_layout layout, void *h_save, void *out,
@@ -174,7 +176,8 @@ moe_status moe_expert_forward(const moe_metadata *meta, const void *x, const voi
  *   invalid slots (issue #68, question 4: gradients for routing scores returned
  *   in [N_recv,K] layout).
  * h_saved is the h_save written by the forward with the same metadata.
- * topk_idx is the [N,K] array the metadata was built from. */
+ * topk_idx is the [N,K] array the metadata was built from. H and I as for the
+ * forward. */
 moe_status moe_expert_backward(const moe_metadata *meta, const int32_t *topk_idx,
                                const void *x, const void *w_up, const void *w_down,
                                const void *h_saved, const void *dout, int32_t H, int32_t I,

@@ -323,6 +323,12 @@ static void argument_errors() {
   Buf fw(fws);
   EXPECT(moe_expert_forward(&M.m, x.p, wu.p, wd.p, 100, 128, MOE_BF16, MOE_GATEUP_INTERLEAVED,
                             h.p, out.p, fw.p, fws, nullptr),
+         MOE_EUNSUPPORTED);  // H not a multiple of 8
+  EXPECT(moe_expert_forward(&M.m, x.p, wu.p, wd.p, 128, 12, MOE_FP32, MOE_GATEUP_INTERLEAVED,
+                            h.p, out.p, fw.p, fws, nullptr),
+         MOE_EUNSUPPORTED);  // I not a multiple of 8
+  EXPECT(moe_expert_forward(&M.m, x.p, wu.p, wd.p, 128, 0, MOE_BF16, MOE_GATEUP_INTERLEAVED,
+                            h.p, out.p, fw.p, fws, nullptr),
          MOE_EUNSUPPORTED);
   EXPECT(moe_expert_forward(&M.m, x.p, wu.p, wd.p, 128, 128, (moe_dtype)7,
                             MOE_GATEUP_INTERLEAVED, h.p, out.p, fw.p, fws, nullptr),
@@ -427,6 +433,8 @@ int main(int argc, char **argv) {
       full_case(64, 4, 8, 100, 256, 384, dt, lay);     // capacity below N*K
       full_case(0, 2, 4, 0, 128, 128, dt, lay);        // N = 0
       full_case(16, 2, 4, 0, 128, 128, dt, lay);       // capacity = 0
+      full_case(50, 4, 5, 200, 200, 72, dt, lay);      // partial edge tiles
+      full_case(9, 2, 3, 18, 8, 8, dt, lay);           // the smallest H and I
     }
   full_case(4, 64, 1024, 256, 128, 128, MOE_BF16, MOE_GATEUP_INTERLEAVED);  // the limits
   full_case(1, 1, 1, 1, 128, 128, MOE_BF16, MOE_GATEUP_INTERLEAVED);

@@ -34,9 +34,9 @@ bool meta_ok(const moe_metadata *m) {
   return true;
 }
 
+// H and I in whole 16-byte bf16 chunks; the GEMM tiles at their edges may be partial
 bool dims_ok(int32_t H, int32_t I) {
-  return H > 0 && I > 0 && H % kGemmBN == 0 && I % kGemmBN == 0 && H <= (1 << 20) &&
-         I <= (1 << 20);
+  return H > 0 && I > 0 && H % 8 == 0 && I % 8 == 0 && H <= (1 << 20) && I <= (1 << 20);
 }
 
 struct FwdWs {
@@ -60,7 +60,7 @@ BwdWs bwd_layout(const moe_metadata *m, int32_t H, int32_t I, moe_dtype dt) {
   w.aw = w.dh + align_up(cap * 2 * I * es);
   w.dxg = w.aw + align_up(cap * I * es);
   w.partial = w.dxg + align_up(cap * H * es);
-  w.total = w.partial + align_up(cap * (size_t)(I / kGemmBN) * sizeof(float));
+  w.total = w.partial + align_up(cap * (size_t)((I + kGemmBN - 1) / kGemmBN) * sizeof(float));
   return w;
 }
 
@@ -365,9 +365,9 @@ moe_status moe_expert_backward(const moe_metadata *meta, const int32_t *topk_idx
   if (dt == MOE_BF16) {  // one dscore partial per column tile of this GEMM
     int bm, bn, bk;
     gemm_tile(kDownBwd, g, &bm, &bn, &bk);
-    g.n_ntiles = I / bn;
+    g.n_ntiles = (I + bn - 1) / bn;
   } else {
-    g.n_ntiles = I / kGemmBN;
+    g.n_ntiles = (I + kGemmBN - 1) / kGemmBN;
   }
   const int nnt = g.n_ntiles;
   moe_status s = MOE_OK;

@@ -29,6 +29,11 @@
 // [BK][cols+pad], and read with ds_read_b64_tr_b16 (transposing LDS reads), so no
 // operand is transposed in registers (the padding: padc below). Outputs are staged
 // through LDS so every row leaves as whole 128-byte lines.
+//
+// H and I need only be multiples of 8 (one 16-byte chunk). Shapes that leave partial
+// tiles at the column (and reduction, or varlen-K row) edges take 128x128x32 tiles
+// built with RAG, which bound every load and store at those edges without a
+// condition around any memory access.
 #include "common.h"
 #include "kernels.h"
 #include "../../include/moe.h"
@@ -94,7 +99,7 @@ __device__ __forceinline__ bf16x8 frag_mn(const uint16_t *tile, int kbase, int c
 // WGM x WGN waves per workgroup; NT threads. GA (varlen-K): bit 0 = the A rows are
 // gathered through a_rows, bit 1 = the B rows through b_rows (else rows are positions).
 template <int MODE, bool A_KC, bool B_KC, int EPI, int BM, int BN, int BK, int WGM, int WGN,
-          int GA>
+          int GA, bool RAG>
 __global__ __launch_bounds__(64 * WGM * WGN,
                              (BM * BN > 128 * 128) ? (WGM * WGN == 8 ? 2 : 1) : (BK == 32 ? 3 : 2))
 void gemm_bf16_kernel(GemmArgs g) {
@@ -103,6 +108,12 @@ void gemm_bf16_kernel(GemmArgs g) {
   constexpr int TM = WM / 32, TN = WN / 32;    // 32x32 sub-tiles per wave
   constexpr bool SWI = EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_CAT;
   static_assert(TM >= 1 && TN >= 1 && (EPI != EPI_SWIGLU_CAT || TN % 2 == 0), "wave tile");
+  // RAG: the output columns (and, grouped-M, the reduction; varlen-K, the output rows)
+  // need not fill whole tiles, only whole 8-element chunks. Chunks past an edge are
+  // loaded from a clamped in-range address (every load stays unconditional), reduction
+  // chunks past the edge are zeroed when staged, and stores past an edge rewrite the
+  // last in-range chunk with its own bytes.
+  static_assert(!RAG || MODE == VARLEN_K || A_KC, "grouped-M A is reduction-contiguous");
   using AS = TileShape<A_KC, BM, BK>;
   using BS = TileShape<B_KC, BN, BK>;
   constexpr int CPK = BK / 8;  // 16-byte chunks per row of a reduction-contiguous tile
@@ -156,7 +167,7 @@ void gemm_bf16_kernel(GemmArgs g) {
     __syncthreads();
     wave0_exclusive_scan(s_pref, g.E);
     __syncthreads();
-    ntn = g.N / BN;
+    ntn = RAG ? (g.N + BN - 1) / BN : g.N / BN;
     const int G = s_pref[g.E] * ntn;
     const int x = blockIdx.x % kNumXcd, q = G / kNumXcd, rq = G % kNumXcd;
     tstart = x * q + min(x, rq);
@@ -165,7 +176,7 @@ void gemm_bf16_kernel(GemmArgs g) {
     tstep = gridDim.x / kNumXcd;
     if (tl >= tcnt) return;
     decode(tstart + tl, e, nt, row0, rows);
-    nk = g.K / BK;
+    nk = RAG ? (g.K + BK - 1) / BK : g.K / BK;
   } else {
     // Work per tile is the expert's row count, which can be very skewed. Experts are
     // taken largest first, and every XCD gets one contiguous eighth of each expert's
@@ -189,7 +200,8 @@ void gemm_bf16_kernel(GemmArgs g) {
     // columns of its column band, so the bytes all XCDs fetch per reduction row are
     // xb * M + xa * N; the cut with the fewest is taken (ties: more row bands). Grids
     // that no cut divides are dealt out flat.
-    const int mtn = g.M / BM, ntn = g.N / BN, tpe = mtn * ntn;
+    const int mtn = RAG ? (g.M + BM - 1) / BM : g.M / BM;
+    const int ntn = RAG ? (g.N + BN - 1) / BN : g.N / BN, tpe = mtn * ntn;
     int xa = 0, xb = 0;
     for (int a = kNumXcd; a >= 1; a >>= 1) {
       const int b = kNumXcd / a;
@@ -237,7 +249,8 @@ void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < B_LD; i++) {
       if constexpr (B_KC) {
-        const int64_t n = (int64_t)nt_ * BN + tid / CPK + (NT / CPK) * i;
+        int64_t n = (int64_t)nt_ * BN + tid / CPK + (NT / CPK) * i;
+        if constexpr (RAG) n = min(n, (int64_t)g.N - 1);
         b_ptr[i] = B + (int64_t)e_ * g.b_es + n * g.ldb + (tid % CPK) * 8;
       } else {
         constexpr int CPR = BN / 8;  // chunks per k-row
@@ -249,7 +262,14 @@ void gemm_bf16_kernel(GemmArgs g) {
           static_assert((WN / 2) % 8 == 0, "gate/up halves in whole chunks");
           const int c = (tid % CPR) * 8, w = c / WN, cw = c % WN;
           const int jb = nt_ * (BN / 2) + w * (WN / 2);
-          col = cw < WN / 2 ? jb + cw : g.N / 2 + jb + (cw - WN / 2);
+          if constexpr (RAG) {  // pairs past I read the last in-range chunk
+            const int j = min(cw < WN / 2 ? jb + cw : jb + (cw - WN / 2), g.N / 2 - 8);
+            col = cw < WN / 2 ? j : g.N / 2 + j;
+          } else {
+            col = cw < WN / 2 ? jb + cw : g.N / 2 + jb + (cw - WN / 2);
+          }
+        } else if constexpr (RAG) {
+          col = min(col, (int64_t)g.N - 8);
         }
         b_ptr[i] = B + (int64_t)e_ * g.b_es + (int64_t)kr * g.ldb + col;
       }
@@ -291,22 +311,36 @@ void gemm_bf16_kernel(GemmArgs g) {
   do {                                                                                     \
     const int k0 = (k0_);                                                                  \
     if constexpr (MODE == GROUPED_M) {                                                     \
+      /* RAG: a reduction chunk past K reads the row's last chunk (zeroed when staged) */ \
+      const int kc_ = RAG ? min(k0, g.K - 8 - (tid % CPK) * 8) : k0;                       \
       _Pragma("unroll") for (int i = 0; i < A_LD; i++) ra[i] =                             \
-          *(const u32x4 *)(a_row[i] + k0);                                                 \
+          *(const u32x4 *)(a_row[i] + kc_);                                                \
       _Pragma("unroll") for (int i = 0; i < B_LD; i++) {                                   \
-        if constexpr (B_KC)                                                                \
-          rb[i] = *(const u32x4 *)(b_ptr[i] + k0);                                         \
-        else                                                                               \
-          rb[i] = *(const u32x4 *)(b_ptr[i] + (int64_t)k0 * g.ldb);                        \
+        if constexpr (B_KC) {                                                              \
+          rb[i] = *(const u32x4 *)(b_ptr[i] + kc_);                                        \
+        } else {                                                                           \
+          constexpr int CPR_ = BN / 8;                                                     \
+          const int kr_ = RAG ? min(k0, g.K - 1 - (tid / CPR_ + (NT / CPR_) * i)) : k0;    \
+          rb[i] = *(const u32x4 *)(b_ptr[i] + (int64_t)kr_ * g.ldb);                       \
+        }                                                                                  \
       }                                                                                    \
     } else {                                                                               \
       /* rows were looked up two tiles earlier (ia/ib); rows past the segment are zeroed  \
          when the set is stored (a select here would wait for these loads at once) */     \
       constexpr int CPA = BM / 8, CPB = BN / 8;                                            \
-      _Pragma("unroll") for (int i = 0; i < A_LD; i++)                                     \
-        ra[i] = *(const u32x4 *)(A + (int64_t)ia[i] * g.lda + (int64_t)mt * BM + (tid % CPA) * 8); \
-      _Pragma("unroll") for (int i = 0; i < B_LD; i++)                                     \
-        rb[i] = *(const u32x4 *)(B + (int64_t)ib[i] * g.ldb + (int64_t)nt * BN + (tid % CPB) * 8); \
+      if constexpr (RAG) { /* columns past an edge read the last in-range chunk */      \
+        const int ca_ = min(mt * BM + (tid % CPA) * 8, g.M - 8);                           \
+        const int cb_ = min(nt * BN + (tid % CPB) * 8, g.N - 8);                           \
+        _Pragma("unroll") for (int i = 0; i < A_LD; i++)                                   \
+          ra[i] = *(const u32x4 *)(A + (int64_t)ia[i] * g.lda + ca_);                      \
+        _Pragma("unroll") for (int i = 0; i < B_LD; i++)                                   \
+          rb[i] = *(const u32x4 *)(B + (int64_t)ib[i] * g.ldb + cb_);                      \
+      } else {                                                                             \
+        _Pragma("unroll") for (int i = 0; i < A_LD; i++)                                   \
+          ra[i] = *(const u32x4 *)(A + (int64_t)ia[i] * g.lda + (int64_t)mt * BM + (tid % CPA) * 8); \
+        _Pragma("unroll") for (int i = 0; i < B_LD; i++)                                   \
+          rb[i] = *(const u32x4 *)(B + (int64_t)ib[i] * g.ldb + (int64_t)nt * BN + (tid % CPB) * 8); \
+      }                                                                                    \
       MOE_ROWS(ia, ib, k0 + 2 * BK);                                                       \
     }                                                                                      \
   } while (0)
@@ -322,6 +356,15 @@ void gemm_bf16_kernel(GemmArgs g) {
         if (kt_ + tid / CPA + (NT / CPA) * i >= seglen) ra[i] = u32x4{0, 0, 0, 0};         \
       _Pragma("unroll") for (int i = 0; i < B_LD; i++)                                     \
         if (kt_ + tid / CPB + (NT / CPB) * i >= seglen) rb[i] = u32x4{0, 0, 0, 0};         \
+    } else if constexpr (RAG) { /* reduction chunks past K -> 0 */                         \
+      const int kt_ = (tile_) * BK;                                                        \
+      _Pragma("unroll") for (int i = 0; i < A_LD; i++)                                     \
+        if (kt_ + (tid % CPK) * 8 >= g.K) ra[i] = u32x4{0, 0, 0, 0};                       \
+      _Pragma("unroll") for (int i = 0; i < B_LD; i++) {                                   \
+        constexpr int CPB = BN / 8;                                                        \
+        if (B_KC ? kt_ + (tid % CPK) * 8 >= g.K : kt_ + tid / CPB + (NT / CPB) * i >= g.K) \
+          rb[i] = u32x4{0, 0, 0, 0};                                                       \
+      }                                                                                    \
     }                                                                                      \
     _Pragma("unroll") for (int i = 0; i < A_LD; i++) {                                     \
       if constexpr (A_KC) {                                                                \
@@ -584,7 +627,11 @@ void gemm_bf16_kernel(GemmArgs g) {
       // grouped-M rows past the segment store the segment's last row again (the same
       // bytes): every store is issued, so the wait counters stay exact for the next
       // tile's loads already in flight
-      const int row = MODE == GROUPED_M ? min(c / CPR, rows - 1) : c / CPR, ch = c % CPR;
+      int row = MODE == GROUPED_M ? min(c / CPR, rows - 1) : c / CPR, ch = c % CPR;
+      if constexpr (RAG) {  // past an edge: the last in-range row / chunk again
+        if constexpr (MODE == VARLEN_K) row = min(row, g.M - mt * BM - 1);
+        ch = min(ch, (g.N - nt * BN) / 8 - 1);
+      }
       int64_t off;
       if constexpr (MODE == GROUPED_M) {
         off = (int64_t)(row0 + row) * g.ldc;
@@ -654,7 +701,8 @@ void gemm_bf16_kernel(GemmArgs g) {
       for (int i = 0; i < BM * CPR / NT; i++) {
         // rows past the segment store its last row again (the same bytes), so every
         // store is issued and the wait counters stay exact
-        const int c = tid + NT * i, row = min(c / CPR, rows - 1), ch = c % CPR;
+        const int c = tid + NT * i, row = min(c / CPR, rows - 1);
+        const int ch = RAG ? min(c % CPR, (g.N - nt * BN) / 8 - 1) : c % CPR;
         __builtin_nontemporal_store(*(const u32x4 *)(Hst + row * HLD + ch * 8),
                                     (u32x4 *)(Hs + (int64_t)(row0 + row) * g.ldc +
                                               (int64_t)nt * BN + ch * 8));
@@ -668,7 +716,8 @@ void gemm_bf16_kernel(GemmArgs g) {
     constexpr int CPA = BN / 16;
 #pragma unroll
     for (int i = 0; i < BM * CPA / NT; i++) {
-      const int c = tid + NT * i, row = min(c / CPA, rows - 1), ch = c % CPA;
+      const int c = tid + NT * i, row = min(c / CPA, rows - 1);
+      const int ch = RAG ? min(c % CPA, (g.N / 2 - nt * (BN / 2)) / 8 - 1) : c % CPA;
       __builtin_nontemporal_store(*(const u32x4 *)(Hst + row * ALD + ch * 8),
                                     (u32x4 *)(Aout + (int64_t)(row0 + row) * g.ldc2 +
                                               (int64_t)nt * (BN / 2) + ch * 8));
@@ -690,7 +739,8 @@ void gemm_bf16_kernel(GemmArgs g) {
     const bool odd = lane & 1;
     u32x2 hv[8];
     auto h_addr = [&](int mi_, int ni_, int rp) {
-      const int jb_ = nt * BN + wn * WN + ni_ * 32 + (col_l & ~1);
+      int jb_ = nt * BN + wn * WN + ni_ * 32 + (col_l & ~1);
+      if constexpr (RAG) jb_ = min(jb_, g.N - 2);  // columns past N: never stored
       const int r = 2 * rp;
       const int row_ = wm * WM + mi_ * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3) + odd;
       const int64_t s_ = row0 + (row_ < rows ? row_ : 0);
@@ -729,7 +779,7 @@ void gemm_bf16_kernel(GemmArgs g) {
           const float up1 = bf16_to_f32((uint16_t)(h4[1] >> 16));
           const float sg0 = sigmoid_fast(gt0), sg1 = sigmoid_fast(gt1);
           const float av0 = gt0 * sg0 * up0, av1 = gt1 * sg1 * up1;
-          if (row < rows) {
+          if (row < rows && (!RAG || jb < g.N)) {
             pp[rp] += dau0 * av0 + dau1 * av1;
             const float da0 = wq * dau0, da1 = wq * dau1;
             const float dg0 = da0 * up0 * sg0 * (1.0f + gt0 * (1.0f - sg0));
@@ -785,12 +835,13 @@ void gemm_bf16_kernel(GemmArgs g) {
 }
 
 template <int MODE, bool A_KC, bool B_KC, int EPI, int GA = 0>
-hipError_t launch_tiles(int bm, int bn, int bk, int grid, const GemmArgs &g, hipStream_t st) {
+hipError_t launch_tiles(int bm, int bn, int bk, bool rag, int grid, const GemmArgs &g,
+                        hipStream_t st) {
   // grouped-M workgroups are persistent: as many as the chip holds at once (capped
   // by the tile count), rounded up to a multiple of the 8 XCDs
-#define MOE_LAUNCH(BM_, BN_, BK_, WGM_, WGN_)                                                \
-  if (bm == BM_ && bn == BN_ && bk == BK_) {                                              \
-    auto kern = gemm_bf16_kernel<MODE, A_KC, B_KC, EPI, BM_, BN_, BK_, WGM_, WGN_, GA>;    \
+#define MOE_LAUNCH(BM_, BN_, BK_, WGM_, WGN_, RAG_)                                          \
+  if (bm == BM_ && bn == BN_ && bk == BK_ && rag == RAG_) {                               \
+    auto kern = gemm_bf16_kernel<MODE, A_KC, B_KC, EPI, BM_, BN_, BK_, WGM_, WGN_, GA, RAG_>; \
     int blocks = grid;                                                                    \
     if constexpr (MODE == GROUPED_M) {                                                    \
       /* workgroups per CU, a property of the kernel: queried once (a function-local     \
@@ -815,11 +866,12 @@ hipError_t launch_tiles(int bm, int bn, int bk, int grid, const GemmArgs &g, hip
     return hipGetLastError();                                                             \
   }
   if constexpr (MODE == GROUPED_M) {
-    MOE_LAUNCH(32, 128, 64, 1, 2)
+    MOE_LAUNCH(32, 128, 64, 1, 2, false)
   }
-  MOE_LAUNCH(128, 128, 64, 2, 2)
-  MOE_LAUNCH(128, 128, 32, 2, 2)
-  MOE_LAUNCH(256, 256, 32, 2, 4)
+  MOE_LAUNCH(128, 128, 64, 2, 2, false)
+  MOE_LAUNCH(128, 128, 32, 2, 2, false)
+  MOE_LAUNCH(256, 256, 32, 2, 4, false)
+  MOE_LAUNCH(128, 128, 32, 2, 2, true)
 #undef MOE_LAUNCH
   return hipErrorInvalidValue;
 }
@@ -832,31 +884,32 @@ hipError_t launch_gemm_bf16(GemmKind kind, const GemmArgs &g, hipStream_t st) {
   if (grid == 0) return hipSuccess;
   int bm, bn, bk;
   gemm_tile(kind, g, &bm, &bn, &bk);
+  const bool rag = gemm_ragged(kind, g);
   switch (kind) {
     // grouped-M: GA = 1 when the A rows are gathered (x_gather_idx), a compile-time
     // choice like the weight gradients' (the row loads then carry no condition)
     case kUpSwiGLU:
       if (!g.a_rows) return hipErrorInvalidValue;
       if (g.gu_concat)
-        return launch_tiles<GROUPED_M, true, false, EPI_SWIGLU_CAT, 1>(bm, bn, bk, grid, g, st);
-      return launch_tiles<GROUPED_M, true, false, EPI_SWIGLU, 1>(bm, bn, bk, grid, g, st);
+        return launch_tiles<GROUPED_M, true, false, EPI_SWIGLU_CAT, 1>(bm, bn, bk, rag, grid, g, st);
+      return launch_tiles<GROUPED_M, true, false, EPI_SWIGLU, 1>(bm, bn, bk, rag, grid, g, st);
     case kDown:
       if (g.a_rows) return hipErrorInvalidValue;
-      return launch_tiles<GROUPED_M, true, false, EPI_STORE, 0>(bm, bn, bk, grid, g, st);
+      return launch_tiles<GROUPED_M, true, false, EPI_STORE, 0>(bm, bn, bk, rag, grid, g, st);
     case kDownBwd:
       if (!g.a_rows) return hipErrorInvalidValue;
-      return launch_tiles<GROUPED_M, true, true, EPI_DSWIGLU, 1>(bm, bn, bk, grid, g, st);
+      return launch_tiles<GROUPED_M, true, true, EPI_DSWIGLU, 1>(bm, bn, bk, rag, grid, g, st);
     case kUpBwd:
       if (g.a_rows) return hipErrorInvalidValue;
-      return launch_tiles<GROUPED_M, true, true, EPI_STORE, 0>(bm, bn, bk, grid, g, st);
+      return launch_tiles<GROUPED_M, true, true, EPI_STORE, 0>(bm, bn, bk, rag, grid, g, st);
     case kWeightGrad:
       // the gathered operand is a compile-time choice: the row-index loads of the loop
       // then carry no condition. Each weight gradient gathers exactly one operand
       // (x rows for dW_up, dout rows for dW_down); other combinations are not built.
       if (g.a_rows && !g.b_rows)
-        return launch_tiles<VARLEN_K, false, false, EPI_STORE, 1>(bm, bn, bk, grid, g, st);
+        return launch_tiles<VARLEN_K, false, false, EPI_STORE, 1>(bm, bn, bk, rag, grid, g, st);
       if (g.b_rows && !g.a_rows)
-        return launch_tiles<VARLEN_K, false, false, EPI_STORE, 2>(bm, bn, bk, grid, g, st);
+        return launch_tiles<VARLEN_K, false, false, EPI_STORE, 2>(bm, bn, bk, rag, grid, g, st);
       return hipErrorInvalidValue;
     default:
       return hipErrorInvalidValue;

@@ -37,7 +37,7 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(GemmArgs g) {
     __syncthreads();
     wave0_exclusive_scan(s_pref, g.E);
     __syncthreads();
-    const int ntn = g.N / BN;
+    const int ntn = (g.N + BN - 1) / BN;  // partial edge tiles: every access is bounded
     const int G = s_pref[g.E] * ntn;
     if ((int)blockIdx.x >= G) return;
     const int mtile = blockIdx.x / ntn;
@@ -52,7 +52,7 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(GemmArgs g) {
     rows = min(BM, g.foff[e + 1] - row0);
     kend = g.K;
   } else {
-    const int mtn = g.M / BM, ntn = g.N / BN;
+    const int mtn = (g.M + BM - 1) / BM, ntn = (g.N + BN - 1) / BN;
     e = blockIdx.x / (mtn * ntn);
     const int r = blockIdx.x - e * (mtn * ntn);
     mt = r / ntn;
@@ -76,33 +76,42 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(GemmArgs g) {
       const int s = row0 + r;
       const int64_t gr = ok ? (g.a_rows ? g.a_rows[s] : s) : 0;
 #pragma unroll
-      for (int i = 0; i < 8; i++) As[kk + i][r] = ok ? A[gr * g.lda + k0 + kk + i] : 0.0f;
+      for (int i = 0; i < 8; i++)
+        As[kk + i][r] = ok && k0 + kk + i < g.K ? A[gr * g.lda + k0 + kk + i] : 0.0f;
     } else {  // k-rows of A are m-contiguous
       const int kr = tid >> 4, m = (tid & 15) * 8;
       const int kk = k0 + kr;
       const bool ok = kk < seglen;
       const int64_t gr = ok ? (g.a_rows ? g.a_rows[seg0 + kk] : seg0 + kk) : 0;
 #pragma unroll
-      for (int i = 0; i < 8; i++) As[kr][m + i] = ok ? A[gr * g.lda + (int64_t)mt * BM + m + i] : 0.0f;
+      for (int i = 0; i < 8; i++) {
+        const int mm = mt * BM + m + i;
+        As[kr][m + i] = ok && mm < g.M ? A[gr * g.lda + mm] : 0.0f;
+      }
     }
     // B tile -> Bs[k][n]
     if constexpr (MODE == GROUPED_M && B_KC) {  // weights [N][K]
       const int n = tid >> 1, kk = (tid & 1) * 8;
+      const bool ok = nt * BN + n < g.N;
       const float *src = B + (int64_t)e * g.b_es + ((int64_t)nt * BN + n) * g.ldb + k0 + kk;
 #pragma unroll
-      for (int i = 0; i < 8; i++) Bs[kk + i][n] = src[i];
+      for (int i = 0; i < 8; i++) Bs[kk + i][n] = ok && k0 + kk + i < g.K ? src[i] : 0.0f;
     } else if constexpr (MODE == GROUPED_M) {  // weights [K][N]
       const int kr = tid >> 4, n = (tid & 15) * 8;
+      const bool ok = k0 + kr < g.K;
       const float *row = B + (int64_t)e * g.b_es + (int64_t)(k0 + kr) * g.ldb;
       if (EPI == EPI_SWIGLU && g.gu_concat) {  // tile column c holds gate/up of pair c/2
 #pragma unroll
         for (int i = 0; i < 8; i++) {
           const int c = nt * BN + n + i;
-          Bs[kr][n + i] = row[(c & 1) ? g.N / 2 + (c >> 1) : (c >> 1)];
+          Bs[kr][n + i] = ok && c < g.N ? row[(c & 1) ? g.N / 2 + (c >> 1) : (c >> 1)] : 0.0f;
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < 8; i++) Bs[kr][n + i] = row[(int64_t)nt * BN + n + i];
+        for (int i = 0; i < 8; i++) {
+          const int c = nt * BN + n + i;
+          Bs[kr][n + i] = ok && c < g.N ? row[c] : 0.0f;
+        }
       }
     } else {
       const int kr = tid >> 4, n = (tid & 15) * 8;
@@ -110,7 +119,10 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(GemmArgs g) {
       const bool ok = kk < seglen;
       const int64_t gr = ok ? (g.b_rows ? g.b_rows[seg0 + kk] : seg0 + kk) : 0;
 #pragma unroll
-      for (int i = 0; i < 8; i++) Bs[kr][n + i] = ok ? B[gr * g.ldb + (int64_t)nt * BN + n + i] : 0.0f;
+      for (int i = 0; i < 8; i++) {
+        const int c = nt * BN + n + i;
+        Bs[kr][n + i] = ok && c < g.N ? B[gr * g.ldb + c] : 0.0f;
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -139,10 +151,14 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(GemmArgs g) {
         if (row >= rows) continue;
         off = (int64_t)(row0 + row) * g.ldc;
       } else {
+        if (mt * BM + row >= g.M) continue;
         off = (int64_t)e * g.c_es + (int64_t)(mt * BM + row) * g.ldc;
       }
 #pragma unroll
-      for (int j = 0; j < 8; j++) C[off + (int64_t)nt * BN + tx * 8 + j] = acc[i][j];
+      for (int j = 0; j < 8; j++) {
+        const int c = nt * BN + tx * 8 + j;
+        if (c < g.N) C[off + c] = acc[i][j];
+      }
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
     float *Hs = (float *)g.C;
@@ -155,6 +171,7 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(GemmArgs g) {
 #pragma unroll
       for (int p = 0; p < 4; p++) {
         const int col = nt * BN + tx * 8 + 2 * p;
+        if (col >= g.N) continue;
         const float gt = acc[i][2 * p], up = acc[i][2 * p + 1];
         if (Hs) {
           Hs[s * g.ldc + col] = gt;
@@ -177,6 +194,7 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(GemmArgs g) {
 #pragma unroll
         for (int jj = 0; jj < 8; jj++) {
           const int j = nt * BN + tx * 8 + jj;
+          if (j >= g.N) continue;
           const float gt = Hs[s * g.ldh + 2 * j], up = Hs[s * g.ldh + 2 * j + 1];
           const float dau = acc[i][jj];
           const float sg = sigmoid_f(gt);

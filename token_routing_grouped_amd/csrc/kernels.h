@@ -113,7 +113,9 @@ struct GemmArgs {
 };
 
 constexpr int kGemmBM = 128, kGemmBN = 128, kGemmBK = 64;  // smallest tile; fp32 mode tile
-// bf16 tile shape chosen for a GEMM (BM x BN x BK) and its grid size (-1: too large)
+// bf16 tile shape chosen for a GEMM (BM x BN x BK), whether its edges are partial
+// tiles, and its grid size (-1: too large)
+bool gemm_ragged(GemmKind kind, const GemmArgs &g);
 void gemm_tile(GemmKind kind, const GemmArgs &g, int *bm, int *bn, int *bk);
 int gemm_grid(GemmKind kind, const GemmArgs &g);
 int gemm_grid_f32(GemmKind kind, const GemmArgs &g);

@@ -12,8 +12,19 @@ size_t route_ws_floats(int64_t NK, int E) { return (size_t)(meta_blocks(NK) + 1)
 // the bytes per flop of 128x128), else 128x128; 32x128x64 with two waves when the
 // capacity averages at most 16 rows per expert (decode), so the matrix work per
 // streamed weight byte matches the rows there are and more workgroups stream weights.
+// Shapes whose output columns (and, grouped-M, reduction; varlen-K, output rows) do
+// not fill whole 128-wide tiles take the 128x128x32 tiles with edge handling; H and I
+// are multiples of 8 (one 16-byte chunk) there.
+bool gemm_ragged(GemmKind kind, const GemmArgs &g) {
+  if (kind == kWeightGrad) return g.M % 128 != 0 || g.N % 128 != 0;
+  return g.N % 128 != 0 || g.K % 32 != 0;
+}
+
 void gemm_tile(GemmKind kind, const GemmArgs &g, int *bm, int *bn, int *bk) {
-  if (kind == kWeightGrad) {
+  if (gemm_ragged(kind, g)) {
+    *bm = *bn = 128;
+    *bk = 32;
+  } else if (kind == kWeightGrad) {
     const bool big = g.M % 256 == 0 && g.N % 256 == 0;
     *bm = big ? 256 : 128;
     *bn = big ? 256 : 128;
@@ -31,15 +42,17 @@ void gemm_tile(GemmKind kind, const GemmArgs &g, int *bm, int *bn, int *bk) {
 // when that exceeds the grid limit); grouped-M returns an upper bound of its tiles
 // (row tiles of every expert segment, bounded from the capacity, times column tiles,
 // capped at INT_MAX), and the launch caps its persistent grid at what the chip holds.
+// Partial edge tiles count as tiles.
 int gemm_grid(GemmKind kind, const GemmArgs &g) {
   int bm, bn, bk;
   gemm_tile(kind, g, &bm, &bn, &bk);
+  const int64_t ntn = ((int64_t)g.N + bn - 1) / bn;
   if (kind == kWeightGrad) {
-    const int64_t grid = (int64_t)g.E * (g.M / bm) * (g.N / bn);
+    const int64_t grid = (int64_t)g.E * (((int64_t)g.M + bm - 1) / bm) * ntn;
     return grid > 0x7fffffff ? -1 : (int)grid;
   }
   const int64_t mt = ((int64_t)g.cap + (int64_t)g.E * (bm - 1)) / bm;
-  const int64_t tiles = mt * (g.N / bn);
+  const int64_t tiles = mt * ntn;
   return tiles > 0x7fffffff ? 0x7fffffff : (int)tiles;
 }
 
@@ -48,11 +61,12 @@ int gemm_grid(GemmKind kind, const GemmArgs &g) {
 // -1 when that exceeds the grid limit.
 int gemm_grid_f32(GemmKind kind, const GemmArgs &g) {
   int64_t grid;
+  const int64_t ntn = ((int64_t)g.N + kGemmBN - 1) / kGemmBN;
   if (kind == kWeightGrad) {
-    grid = (int64_t)g.E * (g.M / kGemmBM) * (g.N / kGemmBN);
+    grid = (int64_t)g.E * (((int64_t)g.M + kGemmBM - 1) / kGemmBM) * ntn;
   } else {
     const int64_t mt = ((int64_t)g.cap + (int64_t)g.E * (kGemmBM - 1)) / kGemmBM;
-    grid = mt * (g.N / kGemmBN);
+    grid = mt * ntn;
   }
   return grid > 0x7fffffff ? -1 : (int)grid;
 }
