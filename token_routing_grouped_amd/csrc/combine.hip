@@ -21,9 +21,11 @@
 namespace moe {
 namespace {
 
-constexpr int CT = 256;    // 4 tokens per workgroup, one wave each
-constexpr int CHUNKS = 4;  // 16-byte chunks per lane per pass over the row
-constexpr int PAIRS = 2;   // pairs whose rows are loaded together
+constexpr int CT = 256;  // 4 tokens per workgroup, one wave each
+// Row split: with few tokens (decode) one wave per token would stream its rows with only a
+// few loads in flight, so the row is cut into column blocks of 64 chunks, one wave each
+// (grid.y), and all of a block's pairs are loaded together.
+constexpr int kSplitTokens = 4096;  // fewer tokens than this take the column blocks
 
 template <typename T>
 struct Vec;
@@ -63,7 +65,9 @@ struct DscoreArgs {
   float *dtw;
 };
 
-template <typename T, bool DSCORE>
+// CHUNKS: 16-byte chunks per lane per pass over the row; PAIRS: pairs whose rows are
+// loaded together; grid.y: column blocks of 64*CHUNKS chunks (1 = whole rows)
+template <typename T, bool DSCORE, int CHUNKS, int PAIRS>
 __global__ __launch_bounds__(CT) void combine_kernel(const T *__restrict__ y,
                                                     const int32_t *__restrict__ tok_off,
                                                     const int32_t *__restrict__ s_rev,
@@ -83,7 +87,7 @@ __global__ __launch_bounds__(CT) void combine_kernel(const T *__restrict__ y,
 
   const int nchunk = H / V;
   u32x4 *orow = (u32x4 *)(out + (int64_t)t * H);
-  for (int c0 = 0; c0 < nchunk; c0 += 64 * CHUNKS) {
+  for (int c0 = blockIdx.y * 64 * CHUNKS; c0 < nchunk; c0 += gridDim.y * 64 * CHUNKS) {
     float acc[CHUNKS][V];
 #pragma unroll
     for (int i = 0; i < CHUNKS; i++)
@@ -119,7 +123,7 @@ __global__ __launch_bounds__(CT) void combine_kernel(const T *__restrict__ y,
     }
   }
 
-  if constexpr (DSCORE) {
+  if (DSCORE && blockIdx.y == 0) {
     const int K = ds.K;
     const int e = lane < K ? ds.topk_idx[(int64_t)t * K + lane] : -1;
     const bool valid = (unsigned)e < (unsigned)ds.E;
@@ -134,22 +138,40 @@ __global__ __launch_bounds__(CT) void combine_kernel(const T *__restrict__ y,
   }
 }
 
+template <typename T, bool DSCORE>
+hipError_t launch_t(const void *y, const int32_t *tok_off, const int32_t *s_rev,
+                    const float *scores, int N, int H, int cap, void *out, const DscoreArgs &ds,
+                    hipStream_t stream) {
+  const int grid = (N + 3) / 4;
+  if (N < kSplitTokens) {
+    constexpr int CH = 1;  // one chunk per lane: a column block is 64 chunks
+    const int nblk = (H / Vec<T>::n + 64 * CH - 1) / (64 * CH);
+    hipLaunchKernelGGL((combine_kernel<T, DSCORE, CH, 8>), dim3(grid, nblk), dim3(CT), 0, stream,
+                       (const T *)y, tok_off, s_rev, scores, N, H, cap, (T *)out, ds);
+  } else {
+    hipLaunchKernelGGL((combine_kernel<T, DSCORE, 4, 2>), dim3(grid), dim3(CT), 0, stream,
+                       (const T *)y, tok_off, s_rev, scores, N, H, cap, (T *)out, ds);
+  }
+  return hipGetLastError();
+}
+
+template <bool DSCORE>
+hipError_t launch(bool bf16, const void *y, const int32_t *tok_off, const int32_t *s_rev,
+                  const float *scores, int N, int H, int cap, void *out, const DscoreArgs &ds,
+                  hipStream_t stream) {
+  if (bf16)
+    return launch_t<uint16_t, DSCORE>(y, tok_off, s_rev, scores, N, H, cap, out, ds, stream);
+  return launch_t<float, DSCORE>(y, tok_off, s_rev, scores, N, H, cap, out, ds, stream);
+}
+
 }  // namespace
 
 hipError_t launch_combine(bool bf16, const void *y, const int32_t *tok_off, const int32_t *s_rev,
                           const float *scores, int N, int H, int cap, void *out,
                           hipStream_t stream) {
   if (N == 0) return hipSuccess;
-  const int grid = (N + 3) / 4;
   DscoreArgs ds = {};
-  if (bf16)
-    hipLaunchKernelGGL((combine_kernel<uint16_t, false>), dim3(grid), dim3(CT), 0, stream,
-                       (const uint16_t *)y, tok_off, s_rev, scores, N, H, cap, (uint16_t *)out,
-                       ds);
-  else
-    hipLaunchKernelGGL((combine_kernel<float, false>), dim3(grid), dim3(CT), 0, stream,
-                       (const float *)y, tok_off, s_rev, scores, N, H, cap, (float *)out, ds);
-  return hipGetLastError();
+  return launch<false>(bf16, y, tok_off, s_rev, scores, N, H, cap, out, ds, stream);
 }
 
 hipError_t launch_combine_dscore(bool bf16, const void *dxg, const int32_t *tok_off,
@@ -157,16 +179,8 @@ hipError_t launch_combine_dscore(bool bf16, const void *dxg, const int32_t *tok_
                                  const int32_t *topk_idx, int K, int E, const float *partial,
                                  int n_ntiles, float *d_topk_weights, hipStream_t stream) {
   if (N == 0) return hipSuccess;
-  const int grid = (N + 3) / 4;
   DscoreArgs ds = {topk_idx, K, E, partial, n_ntiles, d_topk_weights};
-  if (bf16)
-    hipLaunchKernelGGL((combine_kernel<uint16_t, true>), dim3(grid), dim3(CT), 0, stream,
-                       (const uint16_t *)dxg, tok_off, s_rev, nullptr, N, H, cap,
-                       (uint16_t *)dx, ds);
-  else
-    hipLaunchKernelGGL((combine_kernel<float, true>), dim3(grid), dim3(CT), 0, stream,
-                       (const float *)dxg, tok_off, s_rev, nullptr, N, H, cap, (float *)dx, ds);
-  return hipGetLastError();
+  return launch<true>(bf16, dxg, tok_off, s_rev, nullptr, N, H, cap, dx, ds, stream);
 }
 
 }  // namespace moe
