@@ -190,9 +190,12 @@ const char *moe_status_string(moe_status s);
 /* ---- Diagnostics: per-kernel timing with caller-created events ---------------
  * The kernels the three calls enqueue, in launch order. */
 typedef enum {
-  MOE_KERNEL_META_HIST = 0,    /* moe_build_metadata: per-chunk expert histograms */
-  MOE_KERNEL_META_SCAN = 1,    /* moe_build_metadata: prefixes over chunks, totals */
-  MOE_KERNEL_META_SCATTER = 2, /* moe_build_metadata: offsets + stable scatter */
+  MOE_KERNEL_META_HIST = 0,    /* moe_build_metadata: per-chunk expert histograms
+                                  (above 2048 slots) */
+  MOE_KERNEL_META_SCAN = 1,    /* moe_build_metadata: prefixes over chunks, totals
+                                  (above 256 chunks of 512 slots or 34 experts) */
+  MOE_KERNEL_META_SCATTER = 2, /* moe_build_metadata: offsets + stable scatter (up to
+                                  2048 slots: the whole build, counts included) */
   MOE_KERNEL_UP_SWIGLU = 3,    /* forward: gathered up-projection + SwiGLU */
   MOE_KERNEL_DOWN = 4,         /* forward: down projection */
   MOE_KERNEL_COMBINE = 5,      /* forward: weighted combine to [N,H] */

@@ -84,19 +84,22 @@ hipError_t launch_meta_scan(int N, int K, int E, int32_t *ws, hipStream_t, const
   return hipSuccess;
 }
 
-bool meta_fused_scan(int64_t NK, int E) {  // same rule as the library's
+bool meta_fused_scan(int64_t NK, int E) {  // same rules as the library's
   return meta_items(NK) == 2 && E + 2 <= 36 && meta_blocks(NK) <= 256;
 }
+bool meta_solo(int64_t NK) { return NK <= kMetaSoloSlots; }
 
 hipError_t launch_meta_scatter(const int32_t *topk_idx, const float *topk_weights, int N, int K,
                                int E, int capacity, const int32_t *ws, const MetaOut &o,
-                               hipStream_t, bool fused) {
+                               hipStream_t, int mode) {
   g_launches++;
   const int64_t NK = (int64_t)N * K;
   const MetaWs L = meta_ws_layout(NK, E);
   rd(topk_idx, (size_t)NK * 4);
   rd(topk_weights, (size_t)NK * 4);
-  if (fused) {
+  if (mode == kMetaSolo) {  // reads no workspace
+    if (!meta_solo(NK) || o.aux) return hipErrorInvalidValue;
+  } else if (mode == kMetaFused) {
     if (!meta_fused_scan(NK, E) || o.aux) return hipErrorInvalidValue;
     rd(ws + L.hist, (size_t)(E + 2) * L.nblk * 4);
   } else {
@@ -369,12 +372,12 @@ static void argument_errors() {
   // the timing hook's argument checks, and its use around real launches
   void *ev[4] = {(void *)16, (void *)16, (void *)16, nullptr};
   EXPECT(moe_time_kernel((moe_kernel_id)99, ev, 1, nullptr), MOE_EINVAL);
-  EXPECT(moe_time_kernel(MOE_KERNEL_META_HIST, ev, 2, nullptr), MOE_EINVAL);  // a null event
-  EXPECT(moe_time_kernel(MOE_KERNEL_META_HIST, ev, 1, nullptr), MOE_OK);
+  EXPECT(moe_time_kernel(MOE_KERNEL_META_SCATTER, ev, 2, nullptr), MOE_EINVAL);  // a null event
+  EXPECT(moe_time_kernel(MOE_KERNEL_META_SCATTER, ev, 1, nullptr), MOE_OK);
   EXPECT(moe_build_metadata((int32_t *)idx.p, (float *)w.p, &M.m, mws.p, mws_n, nullptr), MOE_OK);
   EXPECT(moe_build_metadata((int32_t *)idx.p, (float *)w.p, &M.m, mws.p, mws_n, nullptr), MOE_OK);
   int32_t n = -1;
-  EXPECT(moe_time_kernel(MOE_KERNEL_META_HIST, nullptr, 0, &n), MOE_OK);
+  EXPECT(moe_time_kernel(MOE_KERNEL_META_SCATTER, nullptr, 0, &n), MOE_OK);
   EXPECT(n, 1);  // the second build's launch was past the one bracketed slot
   if (strcmp(moe_status_string(MOE_ENOSPC), "workspace too small") != 0) exit(4);
   if (strcmp(moe_kernel_name((moe_kernel_id)-1), "unknown") != 0) exit(4);

@@ -139,3 +139,46 @@ def test_slot_count_thresholds_wide_rows(N, K):
     idx[rng.random((N, K)) < 0.2] = -1
     w = rng.standard_normal((N, K)).astype(np.float32)
     check(idx, w, E)
+
+
+@pytest.mark.parametrize("NK,E", [(511, 48), (512, 48), (513, 48), (1024, 48), (1025, 48),
+                                  (2047, 48), (2048, 48), (2049, 48), (600, 1024),
+                                  (2048, 1024)])
+def test_one_workgroup_build_limits(NK, E):
+    """Either side of the slot counts where the whole build runs in one workgroup (four
+    wavefronts up to 512 slots, eight of two rounds up to 1024, eight of four rounds up to
+    2048) and where it takes the multi-chunk launches; up to 1024 experts."""
+    rng = np.random.default_rng(NK + E)
+    idx = rng.integers(0, E, size=(NK, 1)).astype(np.int32)
+    idx[rng.random((NK, 1)) < 0.2] = -1
+    w = rng.standard_normal((NK, 1)).astype(np.float32)
+    check(idx, w, E)
+
+
+@pytest.mark.parametrize("N,K,E", [(8, 8, 32), (64, 8, 1024), (128, 8, 64), (256, 8, 64),
+                                   (257, 8, 64)])
+def test_one_workgroup_build_rows(N, K, E):
+    """Decode-sized batches with K = 8 slots per token, duplicates and -1 slots, bad ids
+    (flagged, treated as -1) and a capacity below P."""
+    rng = np.random.default_rng(N * K + E)
+    idx = rng.integers(0, E, size=(N, K)).astype(np.int32)
+    idx[rng.random((N, K)) < 0.2] = -1
+    w = rng.standard_normal((N, K)).astype(np.float32)
+    got = check(idx, w, E)
+    P = got["P"]
+    if P > 3:
+        check(idx, w, E, capacity=P - 3, expect_status=2)
+    bad = idx.copy()
+    bad[0, 0] = E
+    d = dict(N=N, H=128, I=128, E=E, K=K, topk_idx=bad, topk_weights=w,
+             x=np.zeros((N, 128), np.uint16), w_up=np.zeros((E, 128, 256), np.uint16),
+             w_down=np.zeros((E, 128, 128), np.uint16))
+    clean = np.where(bad < E, bad, -1)
+    ref = oracle.build_metadata(clean, w, E)
+    g = Gpu(d, capacity=max(ref["P"], 1))
+    g.build()
+    m = g.meta_numpy()
+    assert m["status"] == 1
+    for k in KEYS:
+        r = ref[k][:ref["P"]] if k in PAIR_KEYS else ref[k]
+        assert np.array_equal(m[k], r.astype(m[k].dtype)), k

@@ -151,28 +151,32 @@ static MetaOut meta_out(const moe_metadata *meta) {
 }  // namespace moe
 
 namespace {
-// The three metadata launches over an argument-checked metadata object and a workspace
-// of at least meta_workspace_bytes(N*K, E) bytes. None of the workspace needs to start
-// zeroed: every cell the kernels read was written earlier in the same build.
+// The metadata launches (one to three) over an argument-checked metadata object and a
+// workspace of at least meta_workspace_bytes(N*K, E) bytes. None of the workspace needs
+// to start zeroed: every cell the kernels read was written earlier in the same build
+// (the one-launch build reads none).
 moe_status enqueue_metadata(const int32_t *topk_idx, const float *topk_weights,
                             const moe_metadata *meta, int32_t *ws, hipStream_t st) {
   const MetaOut o = meta_out(meta);
-  // few chunks and experts: the scatter pass sums the chunk counts itself (two launches)
-  const bool fused = meta_fused_scan((int64_t)meta->N * meta->K, meta->E);
-  hipError_t err;
-  {
+  const int64_t NK = (int64_t)meta->N * meta->K;
+  // up to 2048 slots: one workgroup builds everything (one launch); few chunks and
+  // experts: the scatter pass sums the chunk counts itself (two launches); else three
+  const int mode = meta_solo(NK) ? kMetaSolo : meta_fused_scan(NK, meta->E) ? kMetaFused
+                                                                           : kMetaScanned;
+  hipError_t err = hipSuccess;
+  if (mode != kMetaSolo) {
     Bracket b(MOE_KERNEL_META_HIST, st);
     err = launch_meta_hist(topk_idx, meta->N, meta->K, meta->E, ws, st);
   }
   if (err != hipSuccess) return MOE_EHIP;
-  if (!fused) {
+  if (mode == kMetaScanned) {
     Bracket b(MOE_KERNEL_META_SCAN, st);
     err = launch_meta_scan(meta->N, meta->K, meta->E, ws, st);
   }
   if (err != hipSuccess) return MOE_EHIP;
   Bracket b(MOE_KERNEL_META_SCATTER, st);
   err = launch_meta_scatter(topk_idx, topk_weights, meta->N, meta->K, meta->E, meta->capacity,
-                            ws, o, st, fused);
+                            ws, o, st, mode);
   return err == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 }  // namespace

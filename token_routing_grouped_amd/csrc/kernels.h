@@ -62,12 +62,18 @@ hipError_t launch_meta_hist(const int32_t *topk_idx, int N, int K, int E, int32_
 // to fsum [E]
 hipError_t launch_meta_scan(int N, int K, int E, int32_t *ws, hipStream_t stream,
                             const float *fcol = nullptr, float *fsum = nullptr);
-// fused: the scatter pass sums the per-chunk counts itself (no scan launch before it);
-// only where meta_fused_scan(N*K, E) holds (few chunks and experts), never for the router
+// Scatter pass modes. kMetaScanned: after the histogram and scan launches. kMetaFused:
+// after the histogram launch only, summing the per-chunk counts itself; where
+// meta_fused_scan(N*K, E) holds (few chunks and experts). kMetaSolo: the whole build in
+// one workgroup (counts included) and no workspace; where meta_solo(N*K) holds. The
+// router's build is always kMetaScanned.
+enum { kMetaScanned = 0, kMetaFused = 1, kMetaSolo = 2 };
+constexpr int64_t kMetaSoloSlots = 2048;  // one workgroup of 512 threads, 4 slots each
 hipError_t launch_meta_scatter(const int32_t *topk_idx, const float *topk_weights, int N, int K,
                                int E, int capacity, const int32_t *ws, const MetaOut &out,
-                               hipStream_t stream, bool fused = false);
+                               hipStream_t stream, int mode = kMetaScanned);
 bool meta_fused_scan(int64_t NK, int E);
+bool meta_solo(int64_t NK);
 
 // ---- router (top-K + the metadata histogram pass, and the aux loss) ---------
 size_t route_ws_floats(int64_t NK, int E);  // per-chunk P sums [E][nblk], then their totals [E]

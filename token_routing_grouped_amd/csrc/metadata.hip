@@ -24,6 +24,8 @@
 //     expert are found with one ballot per expert-id bit and ranked with mbcnt;
 //     per-wave running counts in LDS order the rounds and the four waves. Every
 //     output index is written exactly once.
+// Up to 2048 slots (decode-sized batches) one workgroup holds every slot: it counts
+// them itself and the build is the scatter kernel alone, one launch.
 #include "common.h"
 #include "kernels.h"
 #include "../../include/moe.h"
@@ -152,17 +154,20 @@ __global__ __launch_bounds__(kMetaThreads) void meta_scan_kernel(
   if (tid == 0 && seg == nseg - 1) tot[c] = s_base + t;
 }
 
-// Limits of the scatter pass that scans the chunk counts itself (FUSED): at most
+// Limits of the scatter pass that scans the chunk counts itself (kMetaFused): at most
 // kFusedCols columns per wavefront of a four-wavefront workgroup (E + 2 <= 36) and
 // kFusedChunks chunks, so every count a workgroup needs is loaded at once.
 constexpr int kFusedCols = 9, kFusedChunks = 256;
 
 // NW wavefronts per workgroup; each ranks ITEMS rounds of 64 slots of its share of the
 // chunk (the 2048-slot chunks take 8 wavefronts, so a wavefront's rounds stay at 4).
-// FUSED: `pre` is the per-chunk count columns [E+2][nblk] (nblk = the grid) and `tot` is
-// unused; each workgroup sums the counts of the chunks before its own and of all chunks
-// itself, so the build needs no separate scan launch.
-template <int ITEMS, int NW, bool FUSED>
+// MODE kMetaScanned: `pre` is the chunk's exclusive prefix row, `tot` the column totals.
+// kMetaFused: `pre` is the per-chunk count columns [E+2][nblk] (nblk = the grid) and `tot`
+// is unused; each workgroup sums the counts of the chunks before its own and of all
+// chunks itself, so the build needs no separate scan launch. kMetaSolo: one workgroup
+// holds every slot and counts them itself (LDS integer atomics, as the histogram pass),
+// so the build is this one launch and reads no workspace.
+template <int ITEMS, int NW, int MODE>
 __global__ __launch_bounds__(64 * NW) void meta_scatter_kernel(
     const int32_t *__restrict__ idx, const float *__restrict__ wts, int N, int K, int E,
     int nbits, int cap, const int32_t *__restrict__ pre, const int32_t *__restrict__ tot,
@@ -208,7 +213,25 @@ __global__ __launch_bounds__(64 * NW) void meta_scatter_kernel(
   }
   const bool aux = me == 0 && out.aux;  // router: the load-balancing loss
   float *s_prod = (float *)(s_pq + CHUNK);  // [E] (router only)
-  if constexpr (FUSED) {
+  if constexpr (MODE == kMetaSolo) {
+    for (int c = tid; c < W; c += NT) {
+      s_base[c] = 0;  // no chunk before this one
+      s_off[c] = 0;
+    }
+    __syncthreads();
+    int bad = 0;
+#pragma unroll
+    for (int it = 0; it < ITEMS; it++) {
+      const int e = r_e[it];
+      if ((unsigned)e < (unsigned)E)
+        atomicAdd(&s_off[e], 1);
+      else if (e != -1)
+        bad = 1;
+    }
+    if (bad) atomicOr(&s_off[E + 1], 1);
+    __syncthreads();
+    for (int e = tid; e < E; e += NT) out.expert_frequency[e] = s_off[e];
+  } else if constexpr (MODE == kMetaFused) {
     // wavefront w sums columns w, w + NW, ...: all of its counts are loaded first (one
     // memory round trip), then per column the chunks before this one and all chunks,
     // each by a DPP wavefront scan
@@ -406,38 +429,66 @@ bool meta_fused_scan(int64_t NK, int E) {
   return meta_items(NK) == 2 && E + 2 <= 4 * kFusedCols && meta_blocks(NK) <= kFusedChunks;
 }
 
+bool meta_solo(int64_t NK) { return NK <= kMetaSoloSlots; }
+
 hipError_t launch_meta_scatter(const int32_t *topk_idx, const float *topk_weights, int N, int K,
                                int E, int capacity, const int32_t *ws, const MetaOut &out,
-                               hipStream_t stream, bool fused) {
+                               hipStream_t stream, int mode) {
   const int64_t NK = (int64_t)N * K;
   const MetaWs L = meta_ws_layout(NK, E);
   int nbits = 0;
   while ((1 << nbits) < E) nbits++;
+  if (mode == kMetaSolo) {
+    if (!meta_solo(NK) || out.aux) return hipErrorInvalidValue;
+    // one workgroup: four wavefronts of two rounds of 64 slots up to 512 slots, eight
+    // wavefronts of two rounds up to 1024, of four rounds up to 2048
+#define MOE_SOLO(ITEMS_, NW_)                                                                \
+  {                                                                                        \
+    constexpr int chunk = 64 * (NW_) * (ITEMS_);                                           \
+    const size_t sh =                                                                      \
+        (size_t)(2 * (E + 2) + (NW_) * E + 8 + (E + 1) + 3 * chunk) * sizeof(int32_t);     \
+    static const hipError_t attr = hipFuncSetAttribute(                                    \
+        reinterpret_cast<const void *>(&meta_scatter_kernel<ITEMS_, NW_, kMetaSolo>),      \
+        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);                           \
+    if (attr != hipSuccess) return attr;                                                   \
+    hipLaunchKernelGGL((meta_scatter_kernel<ITEMS_, NW_, kMetaSolo>), dim3(1),             \
+                       dim3(64 * (NW_)), sh, stream, topk_idx, topk_weights, N, K, E, nbits, \
+                       capacity, nullptr, nullptr, out);                                   \
+  }
+    if (NK <= 512)
+      MOE_SOLO(2, 4)
+    else if (NK <= 1024)
+      MOE_SOLO(2, 8)
+    else
+      MOE_SOLO(4, 8)
+#undef MOE_SOLO
+    return hipGetLastError();
+  }
   const int items = meta_items(NK);
   const int nw = items == 8 ? 8 : 4;  // wavefronts of the scatter workgroup
   const size_t sh = (size_t)(2 * (E + 2) + nw * E + 8 + (E + 1) + 3 * meta_chunk(NK) +
                              (out.aux ? E : 0)) * sizeof(int32_t);
-  if (fused) {
+  if (mode == kMetaFused) {
     if (!meta_fused_scan(NK, E) || out.aux) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((meta_scatter_kernel<2, 4, true>), dim3(L.nblk), dim3(64 * 4), sh, stream,
+    hipLaunchKernelGGL((meta_scatter_kernel<2, 4, kMetaFused>), dim3(L.nblk), dim3(64 * 4), sh, stream,
                        topk_idx, topk_weights, N, K, E, nbits, capacity, ws + L.hist, nullptr,
                        out);
   } else if (items == 8) {
     // with 1024 experts the eight waves' running counts take the stage past the 64 KB of
     // dynamic LDS a launch gets by default (a workgroup may use up to 160 KB); set once
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&meta_scatter_kernel<4, 8, false>),
+        reinterpret_cast<const void *>(&meta_scatter_kernel<4, 8, kMetaScanned>),
         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((meta_scatter_kernel<4, 8, false>), dim3(L.nblk), dim3(64 * 8), sh,
+    hipLaunchKernelGGL((meta_scatter_kernel<4, 8, kMetaScanned>), dim3(L.nblk), dim3(64 * 8), sh,
                        stream, topk_idx, topk_weights, N, K, E, nbits, capacity, ws + L.pre,
                        ws + L.tot, out);
   } else if (items == 4)
-    hipLaunchKernelGGL((meta_scatter_kernel<4, 4, false>), dim3(L.nblk), dim3(64 * 4), sh,
+    hipLaunchKernelGGL((meta_scatter_kernel<4, 4, kMetaScanned>), dim3(L.nblk), dim3(64 * 4), sh,
                        stream, topk_idx, topk_weights, N, K, E, nbits, capacity, ws + L.pre,
                        ws + L.tot, out);
   else
-    hipLaunchKernelGGL((meta_scatter_kernel<2, 4, false>), dim3(L.nblk), dim3(64 * 4), sh,
+    hipLaunchKernelGGL((meta_scatter_kernel<2, 4, kMetaScanned>), dim3(L.nblk), dim3(64 * 4), sh,
                        stream, topk_idx, topk_weights, N, K, E, nbits, capacity, ws + L.pre,
                        ws + L.tot, out);
   return hipGetLastError();
