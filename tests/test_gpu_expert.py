@@ -212,3 +212,12 @@ def test_concat_gate_up_layout(dtype, shape):
     for a, b in [(gi.out, gc.out), (gi.h, gc.h), (gi.dw_down, gc.dw_down), (gi.dtw, gc.dtw)]:
         assert np.array_equal(np64(a), np64(b))
     assert np.array_equal(gateup_to_concat(np64(gi.dw_up)), np64(gc.dw_up))
+
+
+@pytest.mark.parametrize("N", [4095, 4096])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_combine_token_count_threshold(dtype, N):
+    """Either side of the token count below which the combine cuts each row into column
+    blocks of 64 chunks, one wavefront each (4096 tokens); H = 136 leaves a partial
+    block, and rows span one or several blocks in the two dtypes."""
+    run_case(synth.case(N=N, H=136, I=128, E=6, K=3, seed=N, p_invalid=0.2), dtype=dtype)
