@@ -48,9 +48,12 @@ def test_noalloc_matches_workspace_build_twice():
 
     big = synth.make_inputs("qwen3_rank", 0, dout=False)
     big_ws = moe.moe_build_metadata_workspace(big["N"], big["K"], big["E"])
+    # 2100 slots: above the 2048 a single workgroup builds without any workspace, so the
+    # second call also runs through the scratch array (five chunks, two launches)
     small = synth.case(N=700, H=128, I=128, E=12, K=3, seed=51, p_invalid=0.3)
     small_ws = moe.moe_build_metadata_workspace(small["N"], small["K"], small["E"])
     assert small_ws < big_ws <= moe.MOE_NOALLOC_SCRATCH_BYTES
+    assert small["N"] * small["K"] > 2048
     print(f"noalloc call 1: N={big['N']} K={big['K']} E={big['E']} ({big_ws} bytes)", flush=True)
     a, b = both_ways(big)
     check_same(a, b, big)
