@@ -438,6 +438,7 @@ int main(int argc, char **argv) {
       full_case(16, 2, 4, 0, 128, 128, dt, lay);       // capacity = 0
       full_case(50, 4, 5, 200, 200, 72, dt, lay);      // partial edge tiles
       full_case(9, 2, 3, 18, 8, 8, dt, lay);           // the smallest H and I
+      full_case(8, 8, 32, 40, 256, 136, dt, lay);      // decode-sized (32-row tiles)
     }
   full_case(4, 64, 1024, 256, 128, 128, MOE_BF16, MOE_GATEUP_INTERLEAVED);  // the limits
   full_case(1, 1, 1, 1, 128, 128, MOE_BF16, MOE_GATEUP_INTERLEAVED);
