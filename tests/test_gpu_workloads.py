@@ -114,3 +114,25 @@ def test_workload(name):
     freq = m["expert_frequency"]
     for e in np.nonzero(freq == 0)[0]:
         assert np.all(np64(g.dw_up[int(e)]) == 0) and np.all(np64(g.dw_down[int(e)]) == 0)
+
+
+@pytest.mark.parametrize("name", ["qwen3_rank", "dsv3_rank"])
+def test_workload_bitwise_repeatable(name):
+    """The whole path twice on the same inputs at the full workload size: every output
+    bit for bit the same (persistent tile walks, XCD rectangles and the per-token combine
+    take no data-dependent order)."""
+    d = synth.make_inputs(name, 0, dout=True)
+    print(f"workload {name}: two full runs", flush=True)
+    res = []
+    for _ in range(2):
+        g = Gpu(d)
+        g.build()
+        g.forward()
+        g.backward()
+        g.torch.cuda.synchronize()
+        res.append([t.clone() for t in (g.out, g.h, g.dx, g.dw_up, g.dw_down, g.dtw)])
+        del g
+    import torch
+    for a, b in zip(*res):
+        bits = {2: torch.int16, 4: torch.int32}[a.element_size()]
+        assert torch.equal(a.contiguous().view(bits), b.contiguous().view(bits))
