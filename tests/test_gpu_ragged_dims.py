@@ -67,3 +67,11 @@ def test_partial_edge_tiles_many_rows():
     """About 2700 rows per expert with H = 2880 / 8 = 360 and I = 184: each persistent
     workgroup walks several ragged tiles, the weight gradients reduce over long segments."""
     run_case(synth.case(N=6000, H=360, I=184, E=8, K=4, seed=46, p_invalid=0.1))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_partial_edge_tiles_max_experts(dtype):
+    """1024 experts (about 14 rows each) with H = 136 and I = 72: the edge-bounded tiles
+    with the largest tile tables and expert ordering, and most weight-gradient tiles
+    partial in both directions."""
+    run_case(synth.case(N=2000, H=136, I=72, E=1024, K=8, seed=47, p_invalid=0.1), dtype=dtype)
