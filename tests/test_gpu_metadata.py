@@ -102,11 +102,13 @@ def test_bad_expert_ids_set_status():
 
 
 @pytest.mark.parametrize("N,K,E", [(300000, 8, 64), (2200000, 1, 7), (140000, 16, 1024),
-                                   (600000, 8, 64), (300000, 16, 1024)])
+                                   (600000, 8, 64), (300000, 16, 1024), (1100000, 8, 64),
+                                   (8400000, 1, 7), (560000, 16, 1024)])
 def test_long_columns_two_pass_scan(N, K, E):
-    """More than 2048 chunks (of 1024 slots at the first three sizes, of 2048 at the
-    last): the column scan runs in segments (a pass of segment sums, then the segments
-    with their bases)."""
+    """Long count columns. From 2048 up to 4096 chunks (of 1024 slots at the first three
+    sizes, of 2048 at the next two) one scan pass with 16 chunks per thread; beyond 4096
+    chunks (the last three, 4102 to 4375 chunks of 2048 slots) the column scan runs in
+    segments: a pass of segment sums, then the segments with their bases."""
     rng = np.random.default_rng(N + K + E)
     idx = rng.integers(0, E, size=(N, K)).astype(np.int32)
     idx[rng.random((N, K)) < 0.25] = -1

@@ -36,7 +36,9 @@ inline int meta_blocks(int64_t NK) {
 // per-chunk exclusive prefixes [nblk][E+2], column totals [E+2], and the segment sums
 // of the two-pass scan for long columns ([2E+2][nseg]: the E+2 count columns, then the
 // router's E probability columns)
-constexpr int kScanSeg = kMetaThreads * 8;  // chunks per scan segment (8 per thread)
+// chunks per scan thread: 8 up to 2048 chunks, else 16 (one pass up to 4096 chunks)
+inline int scan_per(int nblk) { return nblk > kMetaThreads * 8 ? 16 : 8; }
+inline int scan_seg(int nblk) { return kMetaThreads * scan_per(nblk); }  // chunks per segment
 struct MetaWs {
   int nblk, nseg;
   size_t hist, pre, tot, seg, total;
@@ -44,7 +46,7 @@ struct MetaWs {
 inline MetaWs meta_ws_layout(int64_t NK, int E) {
   MetaWs L;
   L.nblk = meta_blocks(NK);
-  L.nseg = (L.nblk + kScanSeg - 1) / kScanSeg;
+  L.nseg = (L.nblk + scan_seg(L.nblk) - 1) / scan_seg(L.nblk);
   const size_t cells = (size_t)L.nblk * (size_t)(E + 2);
   L.hist = 0;
   L.pre = cells;

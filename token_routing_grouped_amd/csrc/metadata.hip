@@ -12,10 +12,10 @@
 //  1. meta_hist: each workgroup counts its chunk per expert (LDS integer atomics),
 //     flags ids outside [-1,E) and counts its valid slots. Columns: E experts,
 //     the flag, the valid count; stored column-major [E+2][nblk].
-//  2. meta_scan: one workgroup per column segment of up to 2048 chunks: exclusive
-//     prefix over chunks (each thread sums 8 consecutive chunks, then DPP scans
-//     inside wavefronts), stored row-major [nblk][E+2], and the column total; long
-//     columns take a first pass of segment sums.
+//  2. meta_scan: one workgroup per column segment of up to 2048 chunks (4096 for longer
+//     columns): exclusive prefix over chunks (each thread sums 8, or 16, consecutive
+//     chunks, then DPP scans inside wavefronts), stored row-major [nblk][E+2], and the
+//     column total; columns of more than 4096 chunks take a first pass of segment sums.
 //  3. meta_scatter: each workgroup reads its row of prefixes and the totals (one
 //     memory round trip; with at most 256 chunks and 34 experts it instead sums the
 //     count columns itself and the scan launch is skipped, a two-launch build), scans
@@ -66,20 +66,20 @@ __global__ __launch_bounds__(kMetaThreads) void meta_hist_kernel(const int32_t *
 
 // Column scans. Column c of hist (c < W) gives pre[b][c] = sum of hist[c][b'] over
 // b' < b and tot[c] = the column's sum; the router's probability columns (c >= W,
-// fcol) only need their sums. A column is cut into segments of kScanSeg chunks, one
-// workgroup each; thread i of a segment covers 8 consecutive chunks, the thread sums
+// fcol) only need their sums. A column is cut into segments of PER * 256 chunks, one
+// workgroup each; thread i of a segment covers PER consecutive chunks, the thread sums
 // are scanned with DPP inside each wavefront and the four wavefront totals in LDS.
 // Columns of more than one segment take two passes: pass 0 writes each segment's
 // sum, pass 1 adds the sums of the earlier segments (in order) as the base.
-template <typename T>
+template <typename T, int PER>
 __device__ __forceinline__ T segment_sum_scan(const T *__restrict__ col, int c0, int n, T *v,
                                               T *run_out, T *s_wave) {
   const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
-  const int b0 = c0 + tid * 8;
+  const int b0 = c0 + tid * PER;
   T s = 0;
 #pragma unroll
-  for (int r = 0; r < 8; r++) {
-    v[r] = (tid * 8 + r < n) ? col[b0 + r] : (T)0;
+  for (int r = 0; r < PER; r++) {
+    v[r] = (tid * PER + r < n) ? col[b0 + r] : (T)0;
     s += v[r];
   }
   T incl;
@@ -101,6 +101,7 @@ __device__ __forceinline__ T segment_sum_scan(const T *__restrict__ col, int c0,
   return total;
 }
 
+template <int PER>
 __global__ __launch_bounds__(kMetaThreads) void meta_scan_kernel(
     const int32_t *__restrict__ hist, int W, int nblk, int nseg, int pass,
     int32_t *__restrict__ pre, int32_t *__restrict__ tot, int32_t *__restrict__ segsum,
@@ -111,8 +112,9 @@ __global__ __launch_bounds__(kMetaThreads) void meta_scan_kernel(
   const int ncol = W + Wf;
   const int c = blockIdx.x % ncol, seg = blockIdx.x / ncol;
   const int tid = threadIdx.x;
-  const int c0 = seg * kScanSeg;
-  const int n = min(kScanSeg, nblk - c0);  // chunks in this segment
+  constexpr int SEG = kMetaThreads * PER;
+  const int c0 = seg * SEG;
+  const int n = min(SEG, nblk - c0);  // chunks in this segment
   if (c >= W) {  // router probability column: fixed-order sums
     const int cf = c - W;
     if (pass == 1 && nseg > 1) {
@@ -123,8 +125,8 @@ __global__ __launch_bounds__(kMetaThreads) void meta_scan_kernel(
       }
       return;
     }
-    float v[8], run;
-    const float t = segment_sum_scan<float>(fcol + (int64_t)cf * nblk, c0, n, v, &run,
+    float v[PER], run;
+    const float t = segment_sum_scan<float, PER>(fcol + (int64_t)cf * nblk, c0, n, v, &run,
                                             (float *)s_wave);
     if (tid == 0) {
       if (nseg > 1) fsegsum[(int64_t)cf * nseg + seg] = t;
@@ -132,9 +134,9 @@ __global__ __launch_bounds__(kMetaThreads) void meta_scan_kernel(
     }
     return;
   }
-  int v[8], run;
+  int v[PER], run;
   const int32_t *col = hist + (int64_t)c * nblk;
-  const int t = segment_sum_scan<int32_t>(col, c0, n, v, &run, s_wave);
+  const int t = segment_sum_scan<int32_t, PER>(col, c0, n, v, &run, s_wave);
   if (pass == 0) {  // segment sums of a long column
     if (tid == 0) segsum[(int64_t)c * nseg + seg] = t;
     return;
@@ -147,8 +149,8 @@ __global__ __launch_bounds__(kMetaThreads) void meta_scan_kernel(
   __syncthreads();
   run += s_base;
 #pragma unroll
-  for (int r = 0; r < 8; r++) {
-    if (tid * 8 + r < n) pre[(int64_t)(c0 + tid * 8 + r) * W + c] = run;
+  for (int r = 0; r < PER; r++) {
+    if (tid * PER + r < n) pre[(int64_t)(c0 + tid * PER + r) * W + c] = run;
     run += v[r];
   }
   if (tid == 0 && seg == nseg - 1) tot[c] = s_base + t;
@@ -414,14 +416,15 @@ hipError_t launch_meta_scan(int N, int K, int E, int32_t *ws, hipStream_t stream
   int32_t *segsum = ws + L.seg;
   float *fsegsum = (float *)(segsum + (size_t)W * L.nseg);
   const dim3 grid((unsigned)((W + Wf) * L.nseg));
+  auto kern = scan_per(L.nblk) == 16 ? meta_scan_kernel<16> : meta_scan_kernel<8>;
   if (L.nseg > 1) {
-    hipLaunchKernelGGL(meta_scan_kernel, grid, dim3(kMetaThreads), 0, stream, ws + L.hist, W,
-                       L.nblk, L.nseg, 0, ws + L.pre, ws + L.tot, segsum, fcol, fsum, fsegsum, Wf);
+    hipLaunchKernelGGL(kern, grid, dim3(kMetaThreads), 0, stream, ws + L.hist, W, L.nblk,
+                       L.nseg, 0, ws + L.pre, ws + L.tot, segsum, fcol, fsum, fsegsum, Wf);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(meta_scan_kernel, grid, dim3(kMetaThreads), 0, stream, ws + L.hist, W,
-                     L.nblk, L.nseg, 1, ws + L.pre, ws + L.tot, segsum, fcol, fsum, fsegsum, Wf);
+  hipLaunchKernelGGL(kern, grid, dim3(kMetaThreads), 0, stream, ws + L.hist, W, L.nblk, L.nseg,
+                     1, ws + L.pre, ws + L.tot, segsum, fcol, fsum, fsegsum, Wf);
   return hipGetLastError();
 }
 
