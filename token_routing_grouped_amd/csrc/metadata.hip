@@ -26,11 +26,27 @@
 //     output index is written exactly once.
 // Up to 2048 slots (decode-sized batches) one workgroup holds every slot: it counts
 // them itself and the build is the scatter kernel alone, one launch.
+#include <atomic>
+
 #include "common.h"
 #include "kernels.h"
 #include "../../include/moe.h"
 
 namespace moe {
+namespace {
+// Lets `fn` use up to 160 KB of dynamic LDS (a launch gets 64 KB by default), once per
+// device: `done` holds one bit per device where it has been set.
+hipError_t allow_large_lds(const void *fn, std::atomic<uint64_t> &done) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  const uint64_t bit = 1ull << dev;
+  if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+  const hipError_t e =
+      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (e == hipSuccess) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
+}  // namespace
 
 template <int ITEMS>
 __global__ __launch_bounds__(kMetaThreads) void meta_hist_kernel(const int32_t *__restrict__ idx,
@@ -450,9 +466,9 @@ hipError_t launch_meta_scatter(const int32_t *topk_idx, const float *topk_weight
     constexpr int chunk = 64 * (NW_) * (ITEMS_);                                           \
     const size_t sh =                                                                      \
         (size_t)(2 * (E + 2) + (NW_) * E + 8 + (E + 1) + 3 * chunk) * sizeof(int32_t);     \
-    static const hipError_t attr = hipFuncSetAttribute(                                    \
-        reinterpret_cast<const void *>(&meta_scatter_kernel<ITEMS_, NW_, kMetaSolo>),      \
-        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);                           \
+    static std::atomic<uint64_t> done{0};                                                  \
+    const hipError_t attr = allow_large_lds(                                               \
+        reinterpret_cast<const void *>(&meta_scatter_kernel<ITEMS_, NW_, kMetaSolo>), done); \
     if (attr != hipSuccess) return attr;                                                   \
     hipLaunchKernelGGL((meta_scatter_kernel<ITEMS_, NW_, kMetaSolo>), dim3(1),             \
                        dim3(64 * (NW_)), sh, stream, topk_idx, topk_weights, N, K, E, nbits, \
@@ -478,10 +494,10 @@ hipError_t launch_meta_scatter(const int32_t *topk_idx, const float *topk_weight
                        out);
   } else if (items == 8) {
     // with 1024 experts the eight waves' running counts take the stage past the 64 KB of
-    // dynamic LDS a launch gets by default (a workgroup may use up to 160 KB); set once
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&meta_scatter_kernel<4, 8, kMetaScanned>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    // dynamic LDS a launch gets by default (a workgroup may use up to 160 KB)
+    static std::atomic<uint64_t> done{0};
+    const hipError_t attr = allow_large_lds(
+        reinterpret_cast<const void *>(&meta_scatter_kernel<4, 8, kMetaScanned>), done);
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL((meta_scatter_kernel<4, 8, kMetaScanned>), dim3(L.nblk), dim3(64 * 8), sh,
                        stream, topk_idx, topk_weights, N, K, E, nbits, capacity, ws + L.pre,
