@@ -148,3 +148,59 @@ def test_noalloc_build_in_a_hip_graph():
             if k in ("x_gather_idx", "s_scatter_idx", "s_reverse_scatter_idx", "router_scores"):
                 got = got[:P]
             assert np.array_equal(got, ref), (rep, k)
+
+
+
+def launches_of(kernel, fn):
+    """How many launches of `kernel` fn enqueues (counted by the timing hook)."""
+    import torch
+
+    import token_routing_grouped_amd as moe
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+    moe.moe_time_kernel(kernel, ev)
+    try:
+        fn()
+        torch.cuda.synchronize()
+    finally:
+        n = moe.moe_time_kernel(kernel, None)
+    return n
+
+
+def test_noalloc_at_the_two_launch_limits():
+    """The allocation-free build through the scratch array at both limits of the
+    two-launch form (256 chunks of 512 slots; 34 experts), with an invalid expert id and
+    capacity below P, and just past each limit (257 chunks; 35 experts), where the column
+    scan is a launch of its own: every call bit-identical to the workspace build, and the
+    scan launched exactly where the limits say."""
+    import torch
+
+    import token_routing_grouped_amd as moe
+
+    cases = [
+        ("256 chunks, 32 experts", dict(N=16384, H=128, I=128, E=32, K=8, seed=71), None, 0),
+        ("34 experts", dict(N=5000, H=128, I=128, E=34, K=6, seed=72, p_invalid=0.2), None, 0),
+        ("257 chunks", dict(N=16385, H=128, I=128, E=32, K=8, seed=73), None, 1),
+        ("35 experts", dict(N=5000, H=128, I=128, E=35, K=6, seed=74), None, 1),
+        ("bad id, capacity below P", dict(N=1000, H=128, I=128, E=20, K=3, seed=75), "err", 0),
+    ]
+    for name, kw, kind, scans in cases:
+        d = synth.case(**kw)
+        cap = None
+        if kind == "err":
+            d["topk_idx"][17, 2] = 40
+            cap = int(((d["topk_idx"] >= 0) & (d["topk_idx"] < kw["E"])).sum()) - 11
+        print(f"noalloc case: {name} N={kw['N']} K={kw['K']} E={kw['E']}", flush=True)
+        a, b = both_ways(d, capacity=cap)
+        if kind == "err":
+            assert a["status"] == b["status"] == 3
+            for k in KEYS:
+                assert np.array_equal(a[k], b[k]), k
+        else:
+            assert b["status"] == 0
+            check_same(a, b, d)
+        g = Gpu(d, capacity=cap)
+        torch.cuda.synchronize()
+        n = launches_of("meta_scan", lambda: moe.moe_build_metadata_noalloc(
+            g.topk_idx, g.topk_weights, g.meta))
+        assert n == scans, name
