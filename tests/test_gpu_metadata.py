@@ -131,6 +131,19 @@ def test_slot_count_thresholds(NK):
     check(idx, w, E)
 
 
+@pytest.mark.parametrize("NK,E", [((1 << 21) - 1, 64), (1 << 21, 64), ((1 << 21) - 1, 300),
+                                  ((1 << 21) - 1, 256), (4000, 256), (4000, 257)])
+def test_ranking_form_thresholds(NK, E):
+    """Either side of the limits up to which the scatter finds a round's same-expert
+    lanes through LDS masks (below 2^21 slots, up to 256 experts) rather than one ballot
+    per expert-id bit: both forms must give the same unique stable order."""
+    rng = np.random.default_rng(NK + E)
+    idx = rng.integers(0, E, size=(NK, 1)).astype(np.int32)
+    idx[rng.random((NK, 1)) < 0.2] = -1
+    w = rng.standard_normal((NK, 1)).astype(np.float32)
+    check(idx, w, E)
+
+
 @pytest.mark.parametrize("N,K", [(32768, 8), (131072, 8)])
 def test_slot_count_thresholds_wide_rows(N, K):
     """The same thresholds reached with K = 8 slots per token (token offsets then come

@@ -16,7 +16,8 @@
 //    gradient and reduces over that expert's rows; empty experts write zeros.
 // Each of the 8 XCDs runs a contiguous run of tiles (tiles of one expert share
 // weights, consecutive column tiles share the gathered rows), which keeps the reuse
-// inside one L2.
+// inside one L2; the weight gradients give each XCD whole experts where the experts'
+// row counts are even enough, else a rectangle of every expert's tiles.
 //
 // Tiles (BM x BN x BK): 256x256x32 with 8 waves (2x4, wave tile 128x64), 128x128 with
 // 4 waves, 32x128x64 with 2 waves; each wave's tile is built from
@@ -211,8 +212,42 @@ void gemm_bf16_kernel(GemmArgs g) {
         xb = b;
       }
     }
+    // Where the experts' row counts are even enough, each XCD takes whole experts instead:
+    // the expert ranks are dealt to the XCDs in a snake (0..7, 7..0, ...), and if no
+    // XCD's rows exceed the mean by more than 1/32 (and the XCDs get equal tile counts),
+    // XCD x runs its experts one after the other, each expert's tiles in groups of up to
+    // four row tiles (column tiles outer within a group). Its 32 tiles in flight then
+    // share the A columns of at most four row tiles and B columns of eight column tiles,
+    // where one rectangle per XCD of a small tile grid reads a band of each operand for
+    // every few tiles.
+    int *s_xrows = s_order + g.E;  // [kNumXcd]
+    if (tid < kNumXcd) {
+      int t = 0;
+      for (int r = 0; r < g.E / kNumXcd; r++)
+        t += s_freq[s_order[r * kNumXcd + ((r & 1) ? kNumXcd - 1 - tid : tid)]];
+      s_xrows[tid] = t;
+    }
+    __syncthreads();
+    bool whole = g.E % kNumXcd == 0;
+    {
+      int64_t mx = 0, sum = 0;
+      for (int x = 0; x < kNumXcd; x++) {
+        mx = max(mx, (int64_t)s_xrows[x]);
+        sum += s_xrows[x];
+      }
+      whole = whole && mx * kNumXcd * 32 <= sum * 33;
+    }
     int rank;
-    if (xa) {
+    if (whole) {
+      const int x = blockIdx.x % kNumXcd, i = blockIdx.x / kNumXcd;
+      const int r = i / tpe, l = i - r * tpe;
+      rank = r * kNumXcd + ((r & 1) ? kNumXcd - 1 - x : x);
+      constexpr int GM = 4;
+      const int gi = l / (GM * ntn), rem = l - gi * GM * ntn;
+      const int gm = min(GM, mtn - gi * GM);
+      nt = rem / gm;
+      mt = gi * GM + (rem - nt * gm);
+    } else if (xa) {
       const int c = tpe / kNumXcd, x = blockIdx.x % kNumXcd, i = blockIdx.x / kNumXcd;
       rank = i / c;
       const int l = i - rank * c, bn = ntn / xb;  // tile l of this XCD's rectangle

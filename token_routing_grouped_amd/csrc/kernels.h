@@ -15,6 +15,19 @@ inline int meta_items(int64_t NK) {
   return NK >= ((int64_t)1 << 22) ? 8 : NK >= ((int64_t)1 << 20) ? 4 : 2;
 }
 inline int meta_chunk(int64_t NK) { return kMetaThreads * meta_items(NK); }
+// The scatter pass ranks a round's lanes per expert through per-wave LDS masks (64-bit
+// words, [waves][E] ahead of its other LDS arrays) up to 256 experts and below 2^21
+// slots; otherwise with one ballot per expert-id bit. Above 2^21 slots the pass is bound
+// by its LDS traffic (the sorted staging), and the masks' three LDS instructions per
+// round cost more than the ballots (measured 2-4 % slower there, 2-4 % faster below).
+constexpr int kMetaMaskExperts = 256;
+constexpr int64_t kMetaMaskSlots = (int64_t)1 << 21;
+constexpr bool meta_use_mask(int64_t NK, int E) {
+  return E <= kMetaMaskExperts && NK < kMetaMaskSlots;
+}
+inline int meta_mask_ints(int64_t NK, int E, int waves) {
+  return meta_use_mask(NK, E) ? 2 * waves * E : 0;
+}
 
 struct MetaOut {
   int32_t *expert_frequency, *expert_frequency_offset, *x_gather_idx, *s_scatter_idx,

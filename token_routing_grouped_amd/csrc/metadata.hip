@@ -21,9 +21,10 @@
 //     count columns itself and the scan launch is skipped, a two-launch build), scans
 //     the totals into expert_frequency_offset, then
 //     ranks its own slots stably: inside a wavefront the lanes holding the same
-//     expert are found with one ballot per expert-id bit and ranked with mbcnt;
-//     per-wave running counts in LDS order the rounds and the four waves. Every
-//     output index is written exactly once.
+//     expert are found through a per-wave LDS mask per expert (up to 256 experts and
+//     below 2^21 slots; else one ballot per expert-id bit) and ranked with mbcnt;
+//     per-wave running counts in LDS order the rounds and the waves. Every output
+//     index is written exactly once.
 // Up to 2048 slots (decode-sized batches) one workgroup holds every slot: it counts
 // them itself and the build is the scatter kernel alone, one launch.
 #include <atomic>
@@ -194,8 +195,11 @@ __global__ __launch_bounds__(64 * NW) void meta_scatter_kernel(
   constexpr int CHUNK = NT * ITEMS;
   static_assert(NW <= 8, "per-wave valid counts");
   extern __shared__ int32_t sh[];
-  int32_t *s_off = sh;              // [E+2]: totals, scanned in place -> offsets, [E] = P,
-                                    // [E+1] = bad-id flags
+  // [NW][E] 64-bit masks of a round's lanes per expert (see meta_use_mask)
+  const bool use_mask = meta_use_mask((int64_t)N * K, E);
+  uint64_t *s_mask = reinterpret_cast<uint64_t *>(sh);
+  // [E+2]: totals, scanned in place -> offsets, [E] = P, [E+1] = bad-id flags
+  int32_t *s_off = sh + (use_mask ? 2 * NW * E : 0);
   int32_t *s_base = s_off + E + 2;  // [E+2]: this chunk's prefix row -> bases
   int32_t *s_run = s_base + E + 2;  // [NW][E] per-wave running counts
   int32_t *s_misc = s_run + NW * E;  // [8]: per-wave valid counts
@@ -296,6 +300,8 @@ __global__ __launch_bounds__(64 * NW) void meta_scatter_kernel(
     }
   }
   for (int i = tid; i < NW * E + 8; i += NT) s_run[i] = 0;
+  if (use_mask)
+    for (int i = tid; i < NW * E; i += NT) s_mask[i] = 0;
   __syncthreads();
   if (aux && tid < kWave) {  // lane-strided partials, then the wave sum: fixed order
     float a = 0.0f;
@@ -328,17 +334,29 @@ __global__ __launch_bounds__(64 * NW) void meta_scatter_kernel(
     const int e = r_e[it];
     const bool v = (unsigned)e < (unsigned)E;
     const uint64_t vm = ballot64(v);
-    // lanes of this round holding the same expert: agree with e on every id bit. Invalid
-    // lanes (e = -1) enter the ballots too but are not in vm, so never in m. Per bit:
-    // m &= bit ? bm : ~bm, as bm ^ (bit - 1) on each 32-bit half (bit - 1 is 0 or all ones)
+    // m: the valid lanes of this round holding the same expert as this lane
     uint64_t m = vm;
-    for (int b = 0; b < nbits; b++) {
-      const uint32_t bit = ((uint32_t)e >> b) & 1u;
-      const uint64_t bm = ballot64(bit != 0u);
-      const uint32_t t = bit - 1u;
-      const uint32_t lo = (uint32_t)m & ((uint32_t)bm ^ t);
-      const uint32_t hi = (uint32_t)(m >> 32) & ((uint32_t)(bm >> 32) ^ t);
-      m = ((uint64_t)hi << 32) | lo;
+    if (use_mask) {
+      // each valid lane ORs its bit into its expert's mask of this wave, reads the mask
+      // back and clears it. A wavefront's LDS instructions execute in issue order, so the
+      // read sees every lane's OR of this round and the clear precedes the next round's
+      // ORs; the OR commutes, so no order among lanes is assumed.
+      uint64_t *mk = s_mask + w * E;
+      if (v) atomicOr(reinterpret_cast<unsigned long long *>(&mk[e]), 1ull << lane);
+      m = v ? mk[e] : 0;
+      if (v) mk[e] = 0;
+    } else {
+      // agree with e on every id bit. Invalid lanes (e = -1) enter the ballots too but
+      // are not in vm, so never in m. Per bit: m &= bit ? bm : ~bm, as bm ^ (bit - 1) on
+      // each 32-bit half (bit - 1 is 0 or all ones)
+      for (int b = 0; b < nbits; b++) {
+        const uint32_t bit = ((uint32_t)e >> b) & 1u;
+        const uint64_t bm = ballot64(bit != 0u);
+        const uint32_t t = bit - 1u;
+        const uint32_t lo = (uint32_t)m & ((uint32_t)bm ^ t);
+        const uint32_t hi = (uint32_t)(m >> 32) & ((uint32_t)(bm >> 32) ^ t);
+        m = ((uint64_t)hi << 32) | lo;
+      }
     }
     int prev = 0;
     if (v) prev = run[e];
@@ -464,8 +482,8 @@ hipError_t launch_meta_scatter(const int32_t *topk_idx, const float *topk_weight
 #define MOE_SOLO(ITEMS_, NW_)                                                                \
   {                                                                                        \
     constexpr int chunk = 64 * (NW_) * (ITEMS_);                                           \
-    const size_t sh =                                                                      \
-        (size_t)(2 * (E + 2) + (NW_) * E + 8 + (E + 1) + 3 * chunk) * sizeof(int32_t);     \
+    const size_t sh = (size_t)(2 * (E + 2) + (NW_) * E + 8 + (E + 1) + 3 * chunk +          \
+                               meta_mask_ints(NK, E, NW_)) * sizeof(int32_t);               \
     static std::atomic<uint64_t> done{0};                                                  \
     const hipError_t attr = allow_large_lds(                                               \
         reinterpret_cast<const void *>(&meta_scatter_kernel<ITEMS_, NW_, kMetaSolo>), done); \
@@ -486,7 +504,7 @@ hipError_t launch_meta_scatter(const int32_t *topk_idx, const float *topk_weight
   const int items = meta_items(NK);
   const int nw = items == 8 ? 8 : 4;  // wavefronts of the scatter workgroup
   const size_t sh = (size_t)(2 * (E + 2) + nw * E + 8 + (E + 1) + 3 * meta_chunk(NK) +
-                             (out.aux ? E : 0)) * sizeof(int32_t);
+                             (out.aux ? E : 0) + meta_mask_ints(NK, E, nw)) * sizeof(int32_t);
   if (mode == kMetaFused) {
     if (!meta_fused_scan(NK, E) || out.aux) return hipErrorInvalidValue;
     hipLaunchKernelGGL((meta_scatter_kernel<2, 4, kMetaFused>), dim3(L.nblk), dim3(64 * 4), sh, stream,
