@@ -197,3 +197,39 @@ def test_one_workgroup_build_rows(N, K, E):
     for k in KEYS:
         r = ref[k][:ref["P"]] if k in PAIR_KEYS else ref[k]
         assert np.array_equal(m[k], r.astype(m[k].dtype)), k
+
+
+@pytest.mark.parametrize("NK", [5000, (1 << 20) + 3, (1 << 22) + 5])
+def test_inputs_with_element_alignment_only(NK):
+    """topk_idx and topk_weights starting 4 bytes past a 16-byte boundary (views one
+    element into larger buffers): the C ABI asks for element alignment only, so the
+    build must give the oracle's metadata bit for bit at each chunk size."""
+    import torch
+
+    import token_routing_grouped_amd as moe
+
+    rng = np.random.default_rng(NK)
+    E = 40
+    idx = rng.integers(0, E, size=(NK, 1)).astype(np.int32)
+    idx[rng.random((NK, 1)) < 0.2] = -1
+    w = rng.standard_normal((NK, 1)).astype(np.float32)
+    print(f"metadata case NK={NK} E={E}, inputs offset by one element", flush=True)
+    ref = oracle.build_metadata(idx, w, E)
+    buf = torch.empty(NK + 4, dtype=torch.int32, device="cuda")
+    ti = buf[1:1 + NK].view(NK, 1)
+    ti.copy_(torch.from_numpy(idx))
+    assert ti.data_ptr() % 16 == 4
+    wbuf = torch.empty(NK + 4, dtype=torch.float32, device="cuda")
+    tw = wbuf[1:1 + NK].view(NK, 1)
+    tw.copy_(torch.from_numpy(w))
+    assert tw.data_ptr() % 16 == 4
+    meta = moe.Metadata(NK, 1, E, NK, device="cuda")
+    moe.moe_build_metadata(ti, tw, meta)
+    torch.cuda.synchronize()
+    P = ref["P"]
+    assert int(meta.status.item()) == 0
+    for k in KEYS:
+        got = getattr(meta, k).cpu().numpy()
+        if k in PAIR_KEYS:
+            got = got[:P]
+        assert np.array_equal(got, ref[k].astype(got.dtype)), k

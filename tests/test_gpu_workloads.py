@@ -1,6 +1,7 @@
 """GPU path at the full workload sizes, in the configuration the benchmark times.
 
-The oracle cannot run these sizes in full, so it computes sampled outputs one by
+The default benchmark workload is also compared in full (test_default_workload_in_full).
+At the larger sizes the oracle cannot run in full, so it computes sampled outputs one by
 one, drawn in strata so that every tile the GPU schedules is checked at least once:
  - h: one row per (expert, 256-row tile) of the sorted positions (every row when the
    layer is small);
@@ -136,3 +137,14 @@ def test_workload_bitwise_repeatable(name):
     for a, b in zip(*res):
         bits = {2: torch.int16, 4: torch.int32}[a.element_size()]
         assert torch.equal(a.contiguous().view(bits), b.contiguous().view(bits))
+
+
+def test_default_workload_in_full():
+    """The default benchmark workload (16384 tokens, H 2048, I 512, 32 experts, top-8,
+    24717 pairs) element by element in full: every element of out, h, dx, dW_up, dW_down
+    and d_topk_weights against the fp64 oracle (about 40 s of oracle time on 16 threads),
+    with the weight gradients on whole experts per XCD, as the benchmark runs them."""
+    from test_gpu_expert import run_case
+
+    d = synth.make_inputs("qwen3_rank", 0, dout=True)
+    run_case(d)
