@@ -32,7 +32,7 @@ def test_decode_sized_concat_layout():
         g.backward()
     tol = TOL["bf16"]
     assert_close(np64(gc.out), f["out"], tol, "out")
-    assert_close(np64(gc.h)[:m["P"]], f["h"], tol, "h_save (interleaved)")
+    assert_close(np64(gc.h[:m["P"]]), f["h"], tol, "h_save (interleaved)")
     assert_close(np64(gc.dw_up), gateup_to_concat(gr["dw_up"]), tol, "dw_up (concat)")
     # the same tiles in the other column order: the forward is bit-identical
     assert np.array_equal(np64(gi.out), np64(gc.out))
@@ -74,4 +74,4 @@ def test_decode_workload_full_forward():
     g.forward()
     tol = TOL["bf16"]
     assert_close(np64(g.out), f["out"], tol, "out")
-    assert_close(np64(g.h)[:m["P"]], f["h"], tol, "h_save")
+    assert_close(np64(g.h[:m["P"]]), f["h"], tol, "h_save")

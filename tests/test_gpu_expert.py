@@ -38,7 +38,7 @@ def run_case(d, dtype="bf16", backward=True, capacity=None):
     errs = {}
     errs["out"] = assert_close(np64(g.out), f["out"], tol, "out")
     P = m["P"]
-    errs["h"] = assert_close(np64(g.h)[:P], f["h"], tol, "h_save")
+    errs["h"] = assert_close(np64(g.h[:P]), f["h"], tol, "h_save")
     if backward:
         g.backward()
         errs["dx"] = assert_close(np64(g.dx), gr["dx"], tol, "dx")
@@ -204,7 +204,7 @@ def test_concat_gate_up_layout(dtype, shape):
         g.backward()
     tol = TOL[dtype]
     assert_close(np64(gc.out), f["out"], tol, "out")
-    assert_close(np64(gc.h)[:m["P"]], f["h"], tol, "h_save (interleaved)")
+    assert_close(np64(gc.h[:m["P"]]), f["h"], tol, "h_save (interleaved)")
     assert_close(np64(gc.dx), gr["dx"], tol, "dx")
     assert_close(np64(gc.dw_up), gateup_to_concat(gr["dw_up"]), tol, "dw_up (concat)")
     assert_close(np64(gc.dw_down), gr["dw_down"], tol, "dw_down")
