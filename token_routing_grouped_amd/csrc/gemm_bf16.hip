@@ -10,8 +10,9 @@
 //    ceil(freq_e/BM) row tiles per expert and finds the (expert, first row, column
 //    tile) of every tile it takes itself, so the launch needs no host sync. The
 //    workgroups are persistent (as many as the chip holds at once) and walk the
-//    tiles of their XCD. Partial row tiles are padded in LDS, never in memory. A
-//    rows are gathered through a row map (x_gather_idx) directly in the tile load.
+//    tiles of their XCD. Partial row tiles are padded in LDS (the padding rows read a
+//    row of zeros), never in memory. A rows are gathered through a row map
+//    (x_gather_idx) directly in the tile load.
 //  - varlen-K (weight gradients): a workgroup owns a BMxBN tile of one expert's
 //    gradient and reduces over that expert's rows; empty experts write zeros.
 // Each of the 8 XCDs runs a contiguous run of tiles (tiles of one expert share
@@ -41,6 +42,10 @@
 
 namespace moe {
 namespace {
+// A row of zeros that padding rows of grouped-M tiles read (static storage starts zeroed
+// and nothing writes it)
+constexpr int kZeroRowElems = 1 << 16;
+__device__ uint16_t g_zero_row[kZeroRowElems];
 
 #ifndef MOE_KC_SWIZZLE
 #define MOE_KC_SWIZZLE 1
@@ -271,16 +276,31 @@ void gemm_bf16_kernel(GemmArgs g) {
   //  mn-contiguous tile of C cols: k-rows (tid / (C/8)) + (256/(C/8))*i, chunk tid % (C/8)
   const uint16_t *a_row[A_LD];
   const uint16_t *b_ptr[B_LD];
-  // pair position of A chunk row i of a tile; rows past the segment re-read the
-  // tile's first row: their accumulator rows are never stored, so need no zeroing
+  // pair position of A chunk row i of a tile (rows past the segment: the tile's first)
   auto a_pos = [&](int i, int row0_, int rows_) {
     const int r = tid / CPK + (NT / CPK) * i;
     return row0_ + (r < rows_ ? r : 0);
   };
+  // memory row m of A chunk row i, stored as -(m + 1) past the segment (where m is the
+  // tile's first row); the row map is read at the clamped position either way (an
+  // unconditional load)
+  auto a_mem = [&](int i, int row0_, int rows_) {
+    const int s_ = a_pos(i, row0_, rows_);
+    const int m_ = (GA & 1) ? g.a_rows[s_] : s_;
+    return tid / CPK + (NT / CPK) * i < rows_ ? m_ : -m_ - 1;
+  };
+  // Rows past the segment read a row of zeros where the reduction fits it (their
+  // accumulator rows are never stored; zeros only spare the matrix cores' power), else
+  // the tile's first row again.
+  const bool zrows = MODE == GROUPED_M && g.K <= kZeroRowElems;
   // row pointers of a tile, from the memory rows of its A chunks
   auto set_ptrs = [&](const int *arow, int e_, int nt_) {
 #pragma unroll
-    for (int i = 0; i < A_LD; i++) a_row[i] = A + (int64_t)arow[i] * g.lda + (tid % CPK) * 8;
+    for (int i = 0; i < A_LD; i++) {
+      const bool pad = arow[i] < 0;
+      const int m_ = pad ? -arow[i] - 1 : arow[i];
+      a_row[i] = (pad && zrows ? g_zero_row : A + (int64_t)m_ * g.lda) + (tid % CPK) * 8;
+    }
 #pragma unroll
     for (int i = 0; i < B_LD; i++) {
       if constexpr (B_KC) {
@@ -313,10 +333,7 @@ void gemm_bf16_kernel(GemmArgs g) {
   int arow[A_LD];  // grouped-M: memory rows of the A chunks of the next tile
   if constexpr (MODE == GROUPED_M) {
 #pragma unroll
-    for (int i = 0; i < A_LD; i++) {
-      const int s_ = a_pos(i, row0, rows);
-      arow[i] = (GA & 1) ? g.a_rows[s_] : s_;
-    }
+    for (int i = 0; i < A_LD; i++) arow[i] = a_mem(i, row0, rows);
     set_ptrs(arow, e, nt);
   }
 
@@ -525,10 +542,7 @@ void gemm_bf16_kernel(GemmArgs g) {
   if constexpr (MODE == GROUPED_M) {
     decode(tstart + min(tl + tstep, tcnt - 1), e_n, nt_n, row0_n, rows_n);
 #pragma unroll
-    for (int i = 0; i < A_LD; i++) {
-      const int s_ = a_pos(i, row0_n, rows_n);
-      arow[i] = (GA & 1) ? g.a_rows[s_] : s_;
-    }
+    for (int i = 0; i < A_LD; i++) arow[i] = a_mem(i, row0_n, rows_n);
   }
   if (nk > 0) {
     if constexpr (MODE == VARLEN_K) {
