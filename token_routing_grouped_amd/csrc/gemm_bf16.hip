@@ -567,32 +567,33 @@ void gemm_bf16_kernel(GemmArgs g) {
     bf16x8 paf[BK / 16][TM], pbf[BK / 16][TN];
     const bool late = __builtin_amdgcn_readfirstlane(wave) >= 4;  // wave-uniform
     // a wave whose rows all lie past the segment (a tile of at most WM rows) skips its
-    // MFMAs: its accumulators stay zero and its rows are never stored
+    // fragment reads and MFMAs (it still stores its share of each stage for the other
+    // group): its accumulators stay zero and its rows are never stored
     constexpr bool SKIP = EPI != EPI_DSWIGLU;
     const bool mm = !SKIP || __builtin_amdgcn_readfirstlane(wm) * WM < rows;
     if (late) MOE_PP_BARRIER();
     int j = 0;
     for (; j + 2 < nk; j += 2) {  // loads past the end re-read the last tile
-      MOE_FRAGS(0);  // tile j
+      if (mm) MOE_FRAGS(0);  // tile j
       MOE_STORE(ra1, rb1, 1, j + 1);
       MOE_LOAD(ra1, rb1, ia1, ib1, kof(j + 3));
       MOE_PP_BARRIER();
       if (mm) MOE_MFMA();
       MOE_PP_BARRIER();
-      MOE_FRAGS(1);  // tile j+1
+      if (mm) MOE_FRAGS(1);  // tile j+1
       MOE_STORE(ra0, rb0, 0, j + 2);
       MOE_LOAD(ra0, rb0, ia0, ib0, kof(j + 4));
       MOE_PP_BARRIER();
       if (mm) MOE_MFMA();
       MOE_PP_BARRIER();
     }
-    MOE_FRAGS(0);  // tile j
+    if (mm) MOE_FRAGS(0);  // tile j
     if (j + 1 < nk) MOE_STORE(ra1, rb1, 1, j + 1);
     MOE_PP_BARRIER();
     if (mm) MOE_MFMA();
     MOE_PP_BARRIER();
     if (j + 1 < nk) {  // tile j+1
-      MOE_FRAGS(1);
+      if (mm) MOE_FRAGS(1);
       MOE_PP_BARRIER();
       if (mm) MOE_MFMA();
       MOE_PP_BARRIER();
