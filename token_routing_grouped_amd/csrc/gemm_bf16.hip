@@ -569,8 +569,7 @@ void gemm_bf16_kernel(GemmArgs g) {
     // a wave whose rows all lie past the segment (a tile of at most WM rows) skips its
     // fragment reads and MFMAs (it still stores its share of each stage for the other
     // group): its accumulators stay zero and its rows are never stored
-    constexpr bool SKIP = EPI != EPI_DSWIGLU;
-    const bool mm = !SKIP || __builtin_amdgcn_readfirstlane(wm) * WM < rows;
+    const bool mm = __builtin_amdgcn_readfirstlane(wm) * WM < rows;
     if (late) MOE_PP_BARRIER();
     int j = 0;
     for (; j + 2 < nk; j += 2) {  // loads past the end re-read the last tile
