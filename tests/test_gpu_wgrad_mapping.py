@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 import synth
+from _util import np64
 from test_gpu_expert import run_case
 
 pytestmark = pytest.mark.gpu
@@ -70,3 +71,13 @@ def test_rectangles_when_experts_not_a_multiple_of_8():
     d = synth.case(N=2000, H=256, I=128, E=12, K=4, seed=84, p_invalid=0.0)
     assert not takes_whole_experts(d)
     run_case(d)
+
+
+def test_whole_experts_per_xcd_all_empty():
+    """Every slot invalid with 16 experts: the XCD totals are all zero, so the whole-expert
+    mapping is taken, and every expert's gradient must still be written as exact zeros."""
+    N, E, K = 300, 16, 4
+    d = synth.case(N=N, H=256, I=128, E=E, K=K, seed=85, topk_idx=-np.ones((N, K), np.int32))
+    assert takes_whole_experts(d)
+    g, _ = run_case(d)
+    assert np.all(np64(g.dw_up) == 0) and np.all(np64(g.dw_down) == 0)
