@@ -212,6 +212,29 @@ def metadata_sweep(moe, synth, torch, np):
                       "unit": "us", "sweep": rows}), flush=True)
 
 
+def token_sweep(moe, synth, torch, np, stream, steps, warmup):
+    """The default workload's step (H 2048, I 512, 32 local experts of 256 global, top-8,
+    the same routing recipe) at other token counts per rank, N = 2^10 .. 2^16: where tile
+    quantisation, launch latency and the fixed per-call work begin to weigh."""
+    base = synth.CONFIGS["qwen3_rank"]
+    rows = []
+    for logn in range(10, 17):
+        name = f"qwen3_rank_n{1 << logn}"
+        synth.CONFIGS[name] = dict(base, N=1 << logn)
+        r, _ = measure(moe, synth, torch, np, name, 0, steps, warmup, 0, stream)
+        r.pop("_handles", None)
+        row = {"N": r["N"], "P": r["P"], "ms_per_step": r["ms_per_step"],
+               "TFLOPs": r["TFLOPs"], "mfma_frac": r["mfma_frac"],
+               "dominant": r["roofline"]["kernel"], "dominant_bound": r["roofline"]["bound"],
+               "dominant_achieved": r["roofline"]["achieved"],
+               "dominant_unit": r["roofline"]["unit"], "dominant_frac": r["roofline"]["frac"],
+               "kernels_us": r["kernels_us"]}
+        rows.append(row)
+        print(json.dumps(row), flush=True)
+    print(json.dumps({"metric": "fwd+bwd step over tokens per rank (H 2048, I 512, E 32, K 8)",
+                      "unit": "TFLOP/s", "sweep": rows}), flush=True)
+
+
 def router_timing(moe, synth, torch, np, N=32768, E=128, K=8, reps=20):
     """moe_route (top-K + weights + aux loss + the metadata) alone, at the routing
     example of the Hysen Labs page (32768 tokens, 128 experts, top-8, fp32 logits):
@@ -463,6 +486,9 @@ def main():
     ap.add_argument("--metadata-sweep", action="store_true",
                     help="instead of the benchmark, time the metadata build alone for "
                          "N = 2^14 .. 2^20 rows at K=8, E=64 (uniform routing, 20%% -1 slots)")
+    ap.add_argument("--token-sweep", action="store_true",
+                    help="instead of the benchmark, time the default workload's step at "
+                         "N = 2^10 .. 2^16 tokens (the --steps and --warmup given)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the benchmark, run a plain device copy of this many MiB "
                          "(reference kernel for scaling HBM traffic counters)")
@@ -498,6 +524,10 @@ def main():
 
     if args.metadata_sweep:
         metadata_sweep(moe, synth, torch, np)
+        return
+    if args.token_sweep:
+        torch.cuda.set_device(torch.device("cuda:0"))
+        token_sweep(moe, synth, torch, np, torch.cuda.current_stream(), args.steps, args.warmup)
         return
 
     dev = torch.device("cuda:0")

@@ -31,7 +31,13 @@ void gemm_tile(GemmKind kind, const GemmArgs &g, int *bm, int *bn, int *bk) {
     *bk = 32;
   } else {
     const bool skinny = (int64_t)g.cap <= 16LL * g.E && g.N % 128 == 0 && g.K % 64 == 0;
-    const bool big = g.N % 256 == 0 && g.K % 32 == 0;
+    bool big = g.N % 256 == 0 && g.K % 32 == 0;
+    if (big && !skinny) {
+      // fewer 256x256 tiles than the chip has CUs (bounded from the capacity): the
+      // 128x128 tiles, four times as many, keep more of the chip busy
+      const int64_t mt = ((int64_t)g.cap + (int64_t)g.E * 255) / 256;
+      if (mt * (g.N / 256) < kGemmFewTiles) big = false;
+    }
     *bm = skinny ? 32 : big ? 256 : 128;
     *bn = skinny ? 128 : big ? 256 : 128;
     *bk = skinny ? 64 : big ? 32 : (g.K % 64 == 0 ? 64 : 32);
