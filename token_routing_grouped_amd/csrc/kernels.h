@@ -135,6 +135,7 @@ struct GemmArgs {
 
 constexpr int kGemmBM = 128, kGemmBN = 128, kGemmBK = 64;  // smallest tile; fp32 mode tile
 constexpr int64_t kGemmFewTiles = 256;  // grouped-M: below this many 256x256 tiles, 128x128
+constexpr int64_t kWgradFewRows = 128;  // varlen-K: below this many rows per expert, 128x128
 // bf16 tile shape chosen for a GEMM (BM x BN x BK), whether its edges are partial
 // tiles, and its grid size (-1: too large)
 bool gemm_ragged(GemmKind kind, const GemmArgs &g);

@@ -25,7 +25,11 @@ void gemm_tile(GemmKind kind, const GemmArgs &g, int *bm, int *bn, int *bk) {
     *bm = *bn = 128;
     *bk = 32;
   } else if (kind == kWeightGrad) {
-    const bool big = g.M % 256 == 0 && g.N % 256 == 0;
+    // few rows per expert: each tile is a short reduction and then a store burst, and the
+    // 128x128 tiles (several workgroups per CU) overlap one tile's stores with another's
+    // loads
+    const bool big = g.M % 256 == 0 && g.N % 256 == 0 &&
+                     (int64_t)g.cap >= kWgradFewRows * (int64_t)g.E;
     *bm = big ? 256 : 128;
     *bn = big ? 256 : 128;
     *bk = 32;
