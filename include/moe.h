@@ -104,8 +104,8 @@ size_t moe_expert_backward_workspace(const moe_metadata *meta, int32_t H, int32_
 /* Builds every array of *meta from topk_idx [N,K] (int32) and topk_weights [N,K]
  * (fp32), and zeroes-then-sets meta->status. The pair count P stays on the
  * device (expert_frequency_offset[E] and num_activated_expert_per_token_offset[N]).
- * Steps: per-block expert histograms by wavefront ballots, a cross-block scan,
- * then a stable counting-sort scatter (Qwen3.6 serving-script notes,
+ * Steps: per-block expert histograms (LDS counters), a cross-block scan, then a
+ * stable counting-sort scatter ranked inside wavefronts (Qwen3.6 serving-script notes,
  * "Optimization (CCCL segmented-sort pattern)", steps 1-3).
  * Requires 1 <= K <= MOE_MAX_TOPK, 1 <= E <= MOE_MAX_EXPERTS, N >= 0,
  * N*K < 2^31, 0 <= capacity. */

@@ -120,8 +120,8 @@ def test_workload(name):
 @pytest.mark.parametrize("name", ["qwen3_rank", "dsv3_rank"])
 def test_workload_bitwise_repeatable(name):
     """The whole path twice on the same inputs at the full workload size: every output
-    bit for bit the same (persistent tile walks, XCD rectangles and the per-token combine
-    take no data-dependent order)."""
+    bit for bit the same (persistent tile walks, the weight gradients' XCD mappings and
+    the per-token combine take no data-dependent order)."""
     d = synth.make_inputs(name, 0, dout=True)
     print(f"workload {name}: two full runs", flush=True)
     res = []
