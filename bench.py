@@ -478,7 +478,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="time only --workload (by default the line also carries a few steps "
-                         "of each other benchmarked workload)")
+                         "of each other benchmarked workload, and of the default workload at "
+                         "1024 and 4096 tokens)")
     ap.add_argument("--other-steps", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--cold-reps", type=int, default=5,
@@ -586,6 +587,23 @@ def main():
             others[name] = ro
             torch.cuda.empty_cache()
         res["workloads"] = others
+        # the default workload at small token counts per rank (where its GEMMs take the
+        # 128x128 tiles): step time and the longest GEMM against its roofline
+        small = []
+        for n in (1024, 4096):
+            name = f"qwen3_rank_n{n}"
+            synth.CONFIGS[name] = dict(synth.CONFIGS["qwen3_rank"], N=n)
+            print(f"bench: {name}", file=sys.stderr, flush=True)
+            ro, _ = measure(moe, synth, torch, np, name, args.seed, args.other_steps, 3, 0,
+                            stream)
+            ro.pop("_handles")
+            small.append({"N": n, "P": ro["P"], "ms_per_step": ro["ms_per_step"],
+                          "TFLOPs": ro["TFLOPs"], "longest_gemm": ro["roofline"]["kernel"],
+                          "bound": ro["roofline"]["bound"],
+                          "achieved": ro["roofline"]["achieved"],
+                          "unit": ro["roofline"]["unit"], "frac": ro["roofline"]["frac"]})
+            torch.cuda.empty_cache()
+        res["qwen3_rank_small_n"] = small
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(d, backward, args.cpu_seconds)
     print(json.dumps(res), flush=True)
