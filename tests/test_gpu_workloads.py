@@ -148,3 +148,15 @@ def test_default_workload_in_full():
 
     d = synth.make_inputs("qwen3_rank", 0, dout=True)
     run_case(d)
+
+
+@pytest.mark.parametrize("n", [1024, 4096])
+def test_default_dims_at_few_tokens_in_full(n):
+    """The default workload's dimensions and routing at 1024 and 4096 tokens, where the
+    grouped GEMMs take 128x128 tiles (fewer 256x256 tiles than CUs) and, at 1024 tokens,
+    so do the weight gradients (under 128 rows per expert): every output and gradient in
+    full against the fp64 oracle."""
+    from test_gpu_expert import run_case
+
+    d = synth.make_inputs(dict(synth.CONFIGS["qwen3_rank"], N=n), 0, dout=True)
+    run_case(d)
