@@ -12,6 +12,9 @@ size_t route_ws_floats(int64_t NK, int E) { return (size_t)(meta_blocks(NK) + 1)
 // the bytes per flop of 128x128), else 128x128; 32x128x64 with two waves when the
 // capacity averages at most 16 rows per expert (decode), so the matrix work per
 // streamed weight byte matches the rows there are and more workgroups stream weights.
+// At few tokens the 128x128 tiles also replace the 256x256 ones where those would
+// number fewer than the CUs (grouped-M) or where the experts average fewer than 128
+// rows (weight gradients).
 // Shapes whose output columns (and, grouped-M, reduction; varlen-K, output rows) do
 // not fill whole 128-wide tiles take the 128x128x32 tiles with edge handling; H and I
 // are multiples of 8 (one 16-byte chunk) there.
