@@ -334,12 +334,12 @@ __global__ __launch_bounds__(64 * NW) void meta_scatter_kernel(
     const int e = r_e[it];
     const bool v = (unsigned)e < (unsigned)E;
     const uint64_t vm = ballot64(v);
-    // m: the valid lanes of this round holding the same expert as this lane
+    // m: the valid lanes among the current 64 slots holding the same expert as this lane
     uint64_t m = vm;
     if (use_mask) {
       // each valid lane ORs its bit into its expert's mask of this wave, reads the mask
       // back and clears it. A wavefront's LDS instructions execute in issue order, so the
-      // read sees every lane's OR of this round and the clear precedes the next round's
+      // read sees every lane's OR for these 64 slots and the clear precedes the next 64's
       // ORs; the OR commutes, so no order among lanes is assumed.
       uint64_t *mk = s_mask + w * E;
       if (v) atomicOr(reinterpret_cast<unsigned long long *>(&mk[e]), 1ull << lane);
